@@ -1,0 +1,141 @@
+"""fp64 CPU oracle of the selective scan (ctypes binding of ``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package. The HIP product path
+never imports it and shares no code with it.
+
+Every function takes the exact values handed to the GPU (float32 arrays that
+hold fp32 or bf16-representable numbers), upcasts them to float64 and returns
+a float64 result.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+ORD_FORWARD, ORD_REVERSE, ORD_COLUMN, ORD_COLUMN_REVERSE = 0, 1, 2, 3
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ``oracle.c`` with gcc (IEEE double throughout, no fast-math)."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", src, "-o", tmp,
+                        "-lm", "-lpthread"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def load(path: Optional[str] = None):
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=False)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    Lg = ctypes.c_long
+    lib.oracle_scan_f64.argtypes = [I, I, I, Lg, Lg, Lg, I, P, P, P, P, P, P, I, P, P, P, I, P, I]
+    lib.oracle_scan_f64.restype = I
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
+         bc_per_direction: bool, H: int = 0, W: int = 0, delta_softplus: bool = True,
+         nthreads: Optional[int] = None, lib=None) -> np.ndarray:
+    """Generic scan: len(orders) directions, merged by sum, optional gate.
+
+    u, delta, z: [batch, dim, L]; B, C: [batch, dstate, L] (shared, token
+    order) or [batch, ndir, dstate, L] (per direction, scan order);
+    A: [ndir, dim, dstate]; Dskip, dt_bias: [ndir, dim] or None.
+    """
+    lib = lib or load()
+    u, delta, z, B, C, A = map(_f64, (u, delta, z, B, C, A))
+    Dskip, dt_bias = _f64(Dskip), _f64(dt_bias)
+    batch, dim, L = u.shape
+    ndir = len(orders)
+    dstate = A.shape[-1]
+    assert delta.shape == u.shape and (z is None or z.shape == u.shape)
+    assert A.shape == (ndir, dim, dstate)
+    if bc_per_direction:
+        assert B.shape == (batch, ndir, dstate, L) and C.shape == B.shape
+    else:
+        assert B.shape == (batch, dstate, L) and C.shape == B.shape
+    for p in (Dskip, dt_bias):
+        assert p is None or p.shape == (ndir, dim)
+    order = np.ascontiguousarray(orders, dtype=np.intc)
+    y = np.empty((batch, dim, L), np.float64)
+    rc = lib.oracle_scan_f64(batch, dim, dstate, L, H, W, ndir, _ptr(order), _ptr(u),
+                             _ptr(delta), _ptr(z), _ptr(B), _ptr(C), int(bc_per_direction),
+                             _ptr(A), _ptr(Dskip), _ptr(dt_bias), int(bool(delta_softplus)),
+                             _ptr(y), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_scan_f64 failed with status %d" % rc)
+    return y
+
+
+def vim_bidir(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None):
+    """Vim: forward + backward over shared u, delta, z, B, C."""
+    return scan(u, delta, z, B, C, A, Dskip, dt_bias, orders=(ORD_FORWARD, ORD_REVERSE),
+                bc_per_direction=False, delta_softplus=delta_softplus, nthreads=nthreads)
+
+
+def cross4(u, delta, z, B, C, A, Dskip, dt_bias, H, W, delta_softplus=True, nthreads=None):
+    """VMamba cross-scan: row-major, reversed, column-major, reversed."""
+    return scan(u, delta, z, B, C, A, Dskip, dt_bias,
+                orders=(ORD_FORWARD, ORD_REVERSE, ORD_COLUMN, ORD_COLUMN_REVERSE),
+                bc_per_direction=True, H=H, W=W, delta_softplus=delta_softplus,
+                nthreads=nthreads)
+
+
+def s6_1d(u, delta, z, B, C, A, Dskip, dt_bias, reverse=False, delta_softplus=True,
+          nthreads=None):
+    """A single direction. A: [dim, dstate]; Dskip, dt_bias: [dim] or None."""
+    A = np.asarray(A)[None]
+    Dskip = None if Dskip is None else np.asarray(Dskip)[None]
+    dt_bias = None if dt_bias is None else np.asarray(dt_bias)[None]
+    return scan(u, delta, z, B, C, A, Dskip, dt_bias,
+                orders=(ORD_REVERSE if reverse else ORD_FORWARD,), bc_per_direction=False,
+                delta_softplus=delta_softplus, nthreads=nthreads)
+
+
+def run_inputs(inp, nthreads=None) -> np.ndarray:
+    """The oracle on a ``workloads.Inputs`` bundle (the workload decides the kind)."""
+    wl = inp.wl
+    if wl.kind == "vim":
+        return vim_bidir(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias,
+                         nthreads=nthreads)
+    return cross4(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias,
+                  wl.H, wl.W, nthreads=nthreads)

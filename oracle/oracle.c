@@ -1,0 +1,235 @@
+/*
+ * oracle.c -- plain fp64 CPU reference of the selective scan (S6) that Vision
+ * Mamba runs forward and backward and VMamba runs in four cross-scan orders.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load or call this library. The HIP
+ * product path never links, imports or calls it, and it shares no code,
+ * header or table with that path.
+ *
+ * Everything below is the sequential definition written out, step by step,
+ * in double precision, with no blocking, fusion or reordering beyond what the
+ * definition states. Sources (all on "Vision Mamba Guide: Efficient
+ * Bidirectional SSM & VMamba", aifetchly blog, unless noted):
+ *
+ *  - Continuous-Time State Space Equations: y = C h + D x, D a scalar skip.
+ *  - Discretization via Zero-Order Hold: A_bar = exp(delta A); B_bar is
+ *    approximated by delta B (the form the page's code uses); recurrence
+ *    h_t = A_bar h_{t-1} + B_bar x_t, read-out y_t = C h_t.
+ *  - The Selective State Space (S6) Mechanism box: delta_t = softplus(...),
+ *    B_t, C_t input dependent, so A_bar and B_bar change with t.
+ *  - PyTorch code, SimpleSelectiveSSM.forward: h starts at zero, A is
+ *    diagonal (one decay per state), B_t and C_t are shared by all channels.
+ *  - 2. The Bidirectional Mamba Block: forward pass over tokens 1..N+1,
+ *    backward pass from N+1 down to 1; gated fusion
+ *    (y_f + y_b) * sigma(z) with sigma the SiLU.
+ *  - VMamba, 1. Cross-Scan Traversal and the CrossScan2D code: four orders
+ *    (row-major, its reverse, column-major, its reverse); 3. Cross-Merge:
+ *    every sequence mapped back to (h, w) and the four maps summed.
+ *
+ * Readings where the pages leave a step open (each one is listed with its
+ * reason in the design notes):
+ *  - D is applied per direction (y_k += D_k u); D = 0 disables it.
+ *  - delta_raw + dt_bias goes through softplus when delta_softplus != 0.
+ *  - Vim directions share u, delta_raw, z, B and C (spatial order); VMamba
+ *    directions share u, delta_raw (spatial order) and have their own B and C,
+ *    stored in each direction's scan order.
+ *  - The gate, when z is given, multiplies the merged sum by z * sigmoid(z).
+ *
+ * Build: gcc -O2 -fPIC -shared oracle.c -o liboracle.so -lm -lpthread
+ * (no -ffast-math: every operation is IEEE double).
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Direction kinds: the order in which a direction visits the tokens. */
+enum { ORD_FORWARD = 0, ORD_REVERSE = 1, ORD_COLUMN = 2, ORD_COLUMN_REVERSE = 3 };
+
+/* Token index (row-major, p = i*W + j) visited at scan step t.
+ * ORD_COLUMN walks down each column from the top, columns left to right,
+ * which is what the page's x.permute(0, 3, 2, 1).reshape(B, L, C) produces. */
+static long visit(int order, long t, long L, long H, long W)
+{
+    switch (order) {
+    case ORD_FORWARD: return t;
+    case ORD_REVERSE: return L - 1 - t;
+    case ORD_COLUMN: return (t % H) * W + t / H;
+    default: { long r = L - 1 - t; return (r % H) * W + r / H; }
+    }
+}
+
+/* softplus(x) = log(1 + e^x), written in the form that neither overflows
+ * nor loses the small result for very negative x. */
+static double softplus(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+typedef struct {
+    int batch, dim, dstate;
+    long L, H, W;
+    int ndir;
+    const int* order;       /* [ndir] */
+    const double *u, *delta, *z, *B, *C, *A, *Dskip, *dt_bias;
+    int bc_per_direction;   /* 0: B, C are [batch][dstate][L] in token order;
+                               1: [batch][ndir][dstate][L] in scan order */
+    int delta_softplus;
+    double* y;
+    /* work split */
+    long unit_begin, unit_end;
+} job_t;
+
+/* One (batch, channel) unit: every direction's recurrence, then the merge
+ * and the gate, for all tokens of that unit. */
+static void run_unit(const job_t* J, long unit, double* h, double* acc)
+{
+    const long b = unit / J->dim, d = unit % J->dim;
+    const long L = J->L, N = J->dstate;
+    const double* u = J->u + (b * J->dim + d) * L;
+    const double* dl = J->delta + (b * J->dim + d) * L;
+    double* y = J->y + (b * J->dim + d) * L;
+
+    for (long p = 0; p < L; ++p) acc[p] = 0.0;
+
+    for (int k = 0; k < J->ndir; ++k) {
+        const double* A = J->A + ((long)k * J->dim + d) * N;
+        const double Dk = J->Dskip ? J->Dskip[(long)k * J->dim + d] : 0.0;
+        const double bias = J->dt_bias ? J->dt_bias[(long)k * J->dim + d] : 0.0;
+        const double *Bk, *Ck;
+        if (J->bc_per_direction) {
+            Bk = J->B + ((long)b * J->ndir + k) * N * L;
+            Ck = J->C + ((long)b * J->ndir + k) * N * L;
+        } else {
+            Bk = J->B + (long)b * N * L;
+            Ck = J->C + (long)b * N * L;
+        }
+        for (long n = 0; n < N; ++n) h[n] = 0.0;           /* zero initial state */
+        for (long t = 0; t < L; ++t) {
+            const long p = visit(J->order[k], t, L, J->H, J->W);
+            /* index of this step's B_t, C_t row entry */
+            const long q = J->bc_per_direction ? t : p;
+            const double x = dl[p] + bias;
+            const double delta = J->delta_softplus ? softplus(x) : x;
+            double yk = 0.0;
+            for (long n = 0; n < N; ++n) {
+                const double Abar = exp(delta * A[n]);              /* exp(delta A) */
+                const double Bbar_x = delta * Bk[n * L + q] * u[p]; /* delta B x */
+                h[n] = Abar * h[n] + Bbar_x;
+                yk += Ck[n * L + q] * h[n];                         /* C_t h_t */
+            }
+            yk += Dk * u[p];                                        /* D x_t */
+            acc[p] += yk;                                           /* merge by sum */
+        }
+    }
+    for (long p = 0; p < L; ++p) {
+        double v = acc[p];
+        if (J->z) {
+            const double zz = J->z[(b * J->dim + d) * L + p];
+            v *= zz / (1.0 + exp(-zz));                             /* SiLU gate */
+        }
+        y[p] = v;
+    }
+}
+
+static void* worker(void* arg)
+{
+    const job_t* J = (const job_t*)arg;
+    double* h = (double*)malloc(sizeof(double) * (size_t)J->dstate);
+    double* acc = (double*)malloc(sizeof(double) * (size_t)J->L);
+    if (!h || !acc) { free(h); free(acc); return (void*)1; }
+    for (long unit = J->unit_begin; unit < J->unit_end; ++unit) run_unit(J, unit, h, acc);
+    free(h);
+    free(acc);
+    return NULL;
+}
+
+/* Generic entry: ndir directions with the given visiting orders.
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
+int oracle_scan_f64(int batch, int dim, int dstate, long L, long H, long W,
+                    int ndir, const int* order, const double* u, const double* delta,
+                    const double* z, const double* B, const double* C, int bc_per_direction,
+                    const double* A, const double* Dskip, const double* dt_bias,
+                    int delta_softplus, double* y, int nthreads)
+{
+    if (batch < 0 || dim < 0 || dstate < 1 || L < 0 || ndir < 1 || !order) return -1;
+    if (batch == 0 || dim == 0 || L == 0) return 0;
+    if (!u || !delta || !B || !C || !A || !y) return -1;
+    for (int k = 0; k < ndir; ++k) {
+        if (order[k] < 0 || order[k] > 3) return -1;
+        if (order[k] >= ORD_COLUMN && (H < 1 || W < 1 || H * W != L)) return -1;
+    }
+    const long units = (long)batch * dim;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > units) nthreads = (int)units;
+    job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) { free(jobs); free(th); return -2; }
+    int rc = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        job_t* J = &jobs[i];
+        J->batch = batch; J->dim = dim; J->dstate = dstate;
+        J->L = L; J->H = H; J->W = W; J->ndir = ndir; J->order = order;
+        J->u = u; J->delta = delta; J->z = z; J->B = B; J->C = C;
+        J->A = A; J->Dskip = Dskip; J->dt_bias = dt_bias;
+        J->bc_per_direction = bc_per_direction; J->delta_softplus = delta_softplus;
+        J->y = y;
+        J->unit_begin = units * i / nthreads;
+        J->unit_end = units * (i + 1) / nthreads;
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) break;
+        started = i;
+    }
+    if (worker(&jobs[0]) != NULL) rc = -2;
+    for (int i = 1; i <= started; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -2;
+    }
+    /* units a failed pthread_create left undone run on this thread */
+    for (int i = started + 1; i < nthreads; ++i)
+        if (worker(&jobs[i]) != NULL) rc = -2;
+    free(jobs);
+    free(th);
+    return rc;
+}
+
+/* Vim bidirectional scan: forward and backward over the same tensors
+ * (B, C: [batch][dstate][L]); A: [2][dim][dstate]; Dskip, dt_bias: [2][dim]. */
+int oracle_vim_bidir_f64(int batch, int dim, int dstate, long L, const double* u,
+                         const double* delta, const double* z, const double* B,
+                         const double* C, const double* A, const double* Dskip,
+                         const double* dt_bias, int delta_softplus, double* y, int nthreads)
+{
+    static const int order[2] = { ORD_FORWARD, ORD_REVERSE };
+    return oracle_scan_f64(batch, dim, dstate, L, 0, 0, 2, order, u, delta, z, B, C, 0,
+                           A, Dskip, dt_bias, delta_softplus, y, nthreads);
+}
+
+/* VMamba four-direction cross-scan on an H x W grid (L = H*W, row-major).
+ * B, C: [batch][4][dstate][L], each direction's rows in its scan order. */
+int oracle_cross4_f64(int batch, int dim, int dstate, long H, long W, const double* u,
+                      const double* delta, const double* z, const double* B,
+                      const double* C, const double* A, const double* Dskip,
+                      const double* dt_bias, int delta_softplus, double* y, int nthreads)
+{
+    static const int order[4] = { ORD_FORWARD, ORD_REVERSE, ORD_COLUMN, ORD_COLUMN_REVERSE };
+    return oracle_scan_f64(batch, dim, dstate, H * W, H, W, 4, order, u, delta, z, B, C, 1,
+                           A, Dskip, dt_bias, delta_softplus, y, nthreads);
+}
+
+/* One direction (reverse = 0: forward, 1: backward) over [batch][dstate][L]
+ * B, C; A: [dim][dstate]; Dskip, dt_bias: [dim]. */
+int oracle_s6_1d_f64(int batch, int dim, int dstate, long L, int reverse, const double* u,
+                     const double* delta, const double* z, const double* B, const double* C,
+                     const double* A, const double* Dskip, const double* dt_bias,
+                     int delta_softplus, double* y, int nthreads)
+{
+    const int order[1] = { reverse ? ORD_REVERSE : ORD_FORWARD };
+    return oracle_scan_f64(batch, dim, dstate, L, 0, 0, 1, order, u, delta, z, B, C, 0,
+                           A, Dskip, dt_bias, delta_softplus, y, nthreads);
+}
