@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of the selective scan on one MI355X.
+
+One step = one call of the full hot path (softplus discretisation, the
+recurrence in every direction, the D skip, the direction merge and the gate)
+over one batch of synthetic inputs already resident in HBM. The default
+workload is the Vim-S 1024x1024 bidirectional scan (batch 8, L 4,097,
+d_inner 768, d_state 16, bf16 activations, fp32 state).
+
+Prints one JSON line: Gtoken*channel/s over the whole job, the achieved
+HBM GB/s on the algorithmic bytes, the roofline of the scan kernel (timed
+with HIP events on the stream it runs on), and the fp64 CPU oracle's rate on
+the host for comparison.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+#: MI355X published peaks
+HBM_PEAK_GBS = 8000.0
+CU = 256
+CLOCK_HZ = 2.4e9
+FP32_LANE_OPS = CU * 128 * CLOCK_HZ       # 157.3 TFLOP/s fp32 vector = 78.6 T lane-FMA/s
+#: VALU issue slots one state update needs at minimum: exp (quarter rate, 4)
+#: + delta*A, (delta*u)*B, the state FMA and the C*h FMA (1 each)
+SLOTS_PER_UPDATE = 8
+UPDATE_PEAK = FP32_LANE_OPS / SLOTS_PER_UPDATE   # 9.83e12 state updates / s
+
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "vision_mamba_selective_amd", "csrc", "vimscan.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=None,
+                   help="index into vision_mamba_selective_amd.workloads.WORKLOADS")
+    p.add_argument("--sets", type=int, default=0,
+                   help="input sets rotated over the steps (0: enough to exceed 768 MB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-channels", type=int, default=0,
+                   help="channels per batch row in the CPU sample (0: whole workload)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="instead of the scan, run torch copies of known size (counter scale)")
+    return p.parse_args()
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, channel) scan is independent; see DESIGN.md for how it would "
+              "shard). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from vision_mamba_selective_amd import workloads as wlm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+
+    if args.copy_probe:
+        return copy_probe(torch, dev)
+
+    import vision_mamba_selective_amd as vms
+
+    idx = wlm.HEADLINE if args.workload is None else args.workload
+    wl = wlm.WORKLOADS[idx]
+    tdt = torch.bfloat16 if wl.dtype == wlm.BF16 else torch.float32
+    print("bench: workload %s" % wl.name, file=sys.stderr, flush=True)
+
+    inp = wlm.make_inputs(wl)
+
+    def up(a, dt):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+
+    set_bytes = wl.algorithmic_bytes() + (wl.tokens_channels * 4 if wl.dtype == wlm.BF16 else 0)
+    nsets = args.sets or max(1, int(np.ceil(768e6 / set_bytes)))
+    sets = []
+    base = dict(u=up(inp.u, tdt), delta=up(inp.delta, tdt), z=up(inp.z, tdt), B=up(inp.B, tdt),
+                C=up(inp.C, tdt), A=up(inp.A, torch.float32), D=up(inp.D, torch.float32),
+                bias=up(inp.dt_bias, torch.float32))
+    for s in range(nsets):
+        t = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
+        t["y"] = torch.empty_like(t["u"])
+        t["ws"] = None
+        need = vms.workspace_bytes(0 if wl.kind == "vim" else 1, wl.batch, wl.dim, wl.seqlen, tdt)
+        if need:
+            t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        sets.append(t)
+
+    def step(t):
+        if wl.kind == "vim":
+            vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
+                               t["bias"], out=t["y"], workspace=t["ws"])
+        else:
+            vms.vmamba_cross_scan4(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], wl.H, wl.W,
+                                   t["D"], t["bias"], out=t["y"], workspace=t["ws"])
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    print("bench: warmup done, timing %d steps over %d input sets" % (args.steps, nsets),
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(sets[i % nsets])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_s = float(np.mean(kern_ms)) * 1e-3
+    ms_per_step = wall * 1e3 / args.steps
+
+    tc = wl.tokens_channels
+    value = tc / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = wl.algorithmic_bytes()
+    hbm_gbs = alg_bytes / kern_avg_s / 1e9
+    updates = wl.state_updates
+    upd_rate = updates / kern_avg_s
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            with open(PROFILE_TRAFFIC) as f:
+                tr = json.load(f)
+            rec = tr.get(wl.name)
+            if rec and rec.get("kernel_sha") == kernel_hash():
+                traffic = rec.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    out = {
+        "metric": "selective-scan Gtoken*ch/s + achieved HBM GB/s (Vim-S, 1024^2, bidir)",
+        "value": round(value, 3),
+        "unit": "Gtoken*ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == wlm.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "kind": wl.kind, "batch": wl.batch, "d_inner": wl.dim,
+                   "d_state": wl.dstate, "seq_len": wl.seqlen, "directions": wl.ndir,
+                   "state_dtype": "f32", "input_sets_rotated": nsets},
+        "hbm_GBps": round(hbm_gbs, 1),
+        "kernel_ms": round(kern_avg_s * 1e3, 5),
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(upd_rate / 1e12, 4),
+            "peak": round(UPDATE_PEAK / 1e12, 4),
+            "unit": "Tupdate/s",
+            "frac": round(upd_rate / UPDATE_PEAK, 4),
+            "traffic": traffic,
+        },
+        "roofline_hbm": {
+            "bound": "hbm",
+            "achieved": round(hbm_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": alg_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, inp, nch):
+    """The fp64 oracle, as it stands, on the host cores of this machine."""
+    import oracle
+    from vision_mamba_selective_amd import workloads as wlm
+
+    sample = inp
+    desc = "whole workload (%d x %d x %d)" % (wl.batch, wl.dim, wl.seqlen)
+    if nch:
+        sample = wlm.channel_subset(inp, list(range(wl.batch)), list(range(min(nch, wl.dim))))
+        desc = "%d of %d channels of every batch row" % (sample.wl.dim, wl.dim)
+    threads = oracle.default_threads()
+    print("bench: cpu baseline on %s with %d threads" % (desc, threads), file=sys.stderr,
+          flush=True)
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.run_inputs(sample, nthreads=threads)
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(sample.wl.tokens_channels / dt / 1e9, 5), "unit": "Gtoken*ch/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
+            "sample": desc + ", fp64, " + cpu + ", " + platform.machine()}
+
+
+def copy_probe(torch, dev):
+    """Plain copies of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters (a copy of N bytes reads N and writes N)."""
+    n = 256 << 20
+    a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

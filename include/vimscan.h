@@ -1,0 +1,150 @@
+/*
+ * vimscan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ * (libvimscan.so).
+ *
+ * The operation is the selective state space scan (S6) as described on
+ * "Vision Mamba Guide: Efficient Bidirectional SSM & VMamba" (aifetchly
+ * blog):
+ *   - section "Discretization via Zero-Order Hold": A_bar = exp(delta A),
+ *     B_bar ~= delta B, h_t = A_bar h_{t-1} + B_bar x_t, y_t = C h_t;
+ *   - section "Continuous-Time State Space Equations": the D x skip term;
+ *   - box "The Selective State Space (S6) Mechanism": delta_t = softplus(.)
+ *     and B_t, C_t change with every token;
+ *   - section "2. The Bidirectional Mamba Block": a forward pass over the
+ *     tokens, a backward pass in reverse order, and the gated fusion
+ *     (y_f + y_b) * silu(z);
+ *   - section "VMamba: 2D Selective Scan (SS2D) and Cross-Scan Traversal":
+ *     four scan orders of an H x W grid (row-major, its reverse,
+ *     column-major, its reverse), merged by summation.
+ * The PyTorch code on the same page fixes A as diagonal (one decay per
+ * state), zero initial state, and B_t, C_t shared by every channel.
+ *
+ * Per direction k, channel d and batch b, with p = pi_k(t) the token visited
+ * at scan step t:
+ *     delta = softplus(delta_raw[b,d,p] + dt_bias[k,d])   (or without softplus)
+ *     h[n]  = exp(delta * A[k,d,n]) * h[n] + delta * B_t[n] * u[b,d,p]
+ *     y_k[b,d,p] = sum_n C_t[n] * h[n] + Dskip[k,d] * u[b,d,p]
+ * and the result is y[b,d,p] = (sum_k y_k[b,d,p]) * silu(z[b,d,p]) (no gate
+ * when z is NULL). State and arithmetic are fp32 whatever the input dtype.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer on the current HIP device,
+ *     owned by the caller (for example PyTorch's caching allocator). The
+ *     library allocates nothing and keeps no pointer after it returns.
+ *   - Activations (u, delta, z, B, C, y) are contiguous, in the dtype given
+ *     by `dtype`; A, Dskip and dt_bias are contiguous fp32.
+ *   - Layout is channel-major: u, delta, z, y are [batch][dim][L].
+ *   - The call is asynchronous: it validates on the host, enqueues the
+ *     kernels on `stream` (a hipStream_t; NULL is the null stream) and
+ *     returns. Faults during execution surface at the caller's next
+ *     synchronisation.
+ *   - Errors are returned as negative status codes, checked before any HIP
+ *     call is made; nothing is enqueued on error. vs_strerror() names a code
+ *     and vs_last_error() gives the calling thread's last detailed message.
+ *   - y must not overlap any input or the workspace (VS_ERR_ALIAS).
+ *   - Thread-safe and re-entrant; calls on different streams are
+ *     independent, provided their y and workspace buffers are distinct.
+ */
+#ifndef VIMSCAN_H
+#define VIMSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VS_ABI_VERSION 1
+
+/* dtype of u, delta, z, B, C and y */
+enum { VS_F32 = 0, VS_BF16 = 1 };
+
+/* status codes */
+enum {
+    VS_OK = 0,
+    VS_ERR_NULL = -1,        /* a required pointer is NULL */
+    VS_ERR_SHAPE = -2,       /* a size is negative, zero where it must not be, or too large */
+    VS_ERR_DTYPE = -3,       /* unknown dtype */
+    VS_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
+    VS_ERR_ALIAS = -5,       /* y overlaps an input or the workspace */
+    VS_ERR_UNSUPPORTED = -6, /* valid but not supported by this build (e.g. dstate > 16) */
+    VS_ERR_HIP = -7,         /* the HIP runtime reported an error (see vs_last_error) */
+    VS_ERR_WORKSPACE = -8    /* workspace missing or smaller than vs_workspace_bytes() */
+};
+
+/* operation kinds for vs_workspace_bytes */
+enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2 };
+
+/* Largest supported state size (the pages use 16 by default and 8 in a test). */
+#define VS_MAX_DSTATE 16
+
+/* Bytes of device workspace an operation needs for its direction merge:
+ * one fp32 partial sum per output element when y is bf16, 0 otherwise (an
+ * fp32 y holds the partial sums itself). Returns 0 for invalid arguments. */
+size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);
+
+/*
+ * Vision Mamba bidirectional scan (forward over tokens 0..L-1 and backward
+ * over L-1..0), fused with softplus discretisation, the D skip, the merge
+ * and the SiLU gate.
+ *   batch, dim     >= 1; dstate in 1..16; seqlen >= 1 (L, tokens)
+ *   u, delta, z    [batch][dim][L]; delta is the raw value before dt_bias and
+ *                  softplus; z may be NULL (no gate)
+ *   B, C           [batch][dstate][L], shared by both directions (token order)
+ *   A              [2][dim][dstate] fp32, direction 0 = forward, 1 = backward
+ *   Dskip, dt_bias [2][dim] fp32, or NULL for zeros
+ *   delta_softplus 1: delta = softplus(delta_raw + dt_bias); 0: no softplus
+ *   y              [batch][dim][L], written completely
+ *   workspace      at least vs_workspace_bytes(VS_OP_VIM_BIDIR, ...) bytes
+ *                  (may be NULL when that is 0); contents on entry are
+ *                  ignored, contents on return are unspecified
+ */
+int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                   const void* u, const void* delta, const void* z, const void* B,
+                   const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                   int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * VMamba four-direction cross-scan of an H x W grid (L = H*W tokens, stored
+ * row-major: token p = i*W + j). Direction 0 visits p = t, 1 visits
+ * p = L-1-t, 2 visits the columns top to bottom, left to right
+ * (p = (t mod H)*W + t div H), 3 is the reverse of 2. The four outputs are
+ * summed, then gated by silu(z) when z is not NULL.
+ *   u, delta, z, y [batch][dim][H][W]
+ *   B, C           [batch][4][dstate][L]: direction k's B_t, C_t stored in
+ *                  its own scan order (entry t is used at scan step t)
+ *   A              [4][dim][dstate]; Dskip, dt_bias [4][dim] or NULL
+ *   workspace      at least vs_workspace_bytes(VS_OP_CROSS4, ...) bytes
+ */
+int vmamba_cross_scan4(int64_t batch, int64_t dim, int64_t dstate, int64_t H, int64_t W,
+                       int dtype, const void* u, const void* delta, const void* z,
+                       const void* B, const void* C, const float* A, const float* Dskip,
+                       const float* dt_bias, int delta_softplus, void* y, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * One direction (reverse = 0: tokens 0..L-1; 1: L-1..0) with the optional
+ * gate, no merge. Same layouts as vim_scan_bidir with A [dim][dstate] and
+ * Dskip, dt_bias [dim] (or NULL). Needs no workspace.
+ */
+int s6_scan_1d(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+               int reverse, const void* u, const void* delta, const void* z, const void* B,
+               const void* C, const float* A, const float* Dskip, const float* dt_bias,
+               int delta_softplus, void* y, void* stream);
+
+/* Static name of a status code ("VS_OK", ...). Never NULL. */
+const char* vs_strerror(int status);
+
+/* The calling thread's last detailed error message ("" if none). The string
+ * stays valid until the thread's next call into the library. */
+const char* vs_last_error(void);
+
+/* VS_ABI_VERSION of the library. */
+int vs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VIMSCAN_H */

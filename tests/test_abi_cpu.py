@@ -1,0 +1,131 @@
+"""The C ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before any HIP call (no
+compute call is made here: there is no GPU in this container)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vimscan.h")
+
+
+@pytest.fixture(scope="module")
+def nat():
+    from vision_mamba_selective_amd import _native
+    return _native
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for required in ("vim_scan_bidir", "vmamba_cross_scan4", "s6_scan_1d", "vs_strerror",
+                     "vs_last_error", "vs_abi_version", "vs_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(nat):
+    raw = ctypes.CDLL(nat.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(raw, name), name
+    assert set(nat.SIGNATURES) == set(header_functions())
+
+
+def test_version_and_strerror(nat):
+    assert nat.lib.vs_abi_version() == 1
+    assert nat.lib.vs_strerror(0) == b"VS_OK"
+    for code, name in [(-1, b"VS_ERR_NULL"), (-2, b"VS_ERR_SHAPE"), (-3, b"VS_ERR_DTYPE"),
+                       (-4, b"VS_ERR_ALIGN"), (-5, b"VS_ERR_ALIAS"), (-6, b"VS_ERR_UNSUPPORTED"),
+                       (-7, b"VS_ERR_HIP"), (-8, b"VS_ERR_WORKSPACE"), (-99, b"VS_ERR_UNKNOWN")]:
+        assert nat.lib.vs_strerror(code) == name
+
+
+def test_workspace_bytes(nat):
+    f = nat.lib.vs_workspace_bytes
+    assert f(0, 8, 768, 4097, nat.VS_BF16) == 8 * 768 * 4097 * 4
+    assert f(1, 8, 384, 4096, nat.VS_BF16) == 8 * 384 * 4096 * 4
+    assert f(0, 8, 768, 4097, nat.VS_F32) == 0          # fp32 y holds the partial sums
+    assert f(2, 8, 768, 4097, nat.VS_BF16) == 0
+    assert f(0, 0, 768, 4097, nat.VS_BF16) == 0
+
+
+# Fake, well-aligned, non-overlapping device addresses: validation must reject
+# the call before it dereferences anything or touches the HIP runtime.
+MB = 1 << 20
+BASE = 1 << 40
+
+
+def fake(i):
+    return BASE + i * 256 * MB
+
+
+def vim_call(nat, **kw):
+    a = dict(batch=2, dim=8, dstate=16, L=33, dtype=nat.VS_BF16, u=fake(0), delta=fake(1),
+             z=fake(2), B=fake(3), C=fake(4), A=fake(5), D=fake(6), bias=fake(7), sp=1,
+             y=fake(8), ws=fake(9), ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return nat.lib.vim_scan_bidir(a["batch"], a["dim"], a["dstate"], a["L"], a["dtype"], a["u"],
+                                  a["delta"], a["z"], a["B"], a["C"], a["A"], a["D"], a["bias"],
+                                  a["sp"], a["y"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(batch=0), -2),
+    (dict(dim=-1), -2),
+    (dict(L=0), -2),
+    (dict(dstate=0), -2),
+    (dict(dstate=17), -6),
+    (dict(u=None), -1),
+    (dict(B=None), -1),
+    (dict(A=None), -1),
+    (dict(y=None), -1),
+    (dict(u=fake(0) + 1), -4),
+    (dict(dtype=0, u=fake(0) + 2), -4),
+    (dict(A=fake(5) + 2), -4),
+    (dict(y=fake(0) + 64), -5),           # y inside u
+    (dict(y=fake(3) - 64), -5),           # y runs into B
+    (dict(ws=None), -8),
+    (dict(ws_bytes=100), -8),
+    (dict(ws=fake(8) + 128), -5),         # workspace overlaps y
+    (dict(ws=fake(1)), -5),               # workspace overlaps delta
+])
+def test_vim_validation(nat, kw, code):
+    assert vim_call(nat, **kw) == code
+    assert nat.lib.vs_last_error() != b""
+
+
+def test_cross4_validation(nat):
+    f = nat.lib.vmamba_cross_scan4
+    args = [fake(0), fake(1), None, fake(3), fake(4), fake(5), None, None, 1, fake(8), fake(9),
+            1 << 30, None]
+    assert f(1, 4, 16, 0, 5, nat.VS_F32, *args) == -2
+    assert f(1, 4, 16, 5, -1, nat.VS_F32, *args) == -2
+    assert f(1, 4, 32, 5, 7, nat.VS_F32, *args) == -6
+    assert f(1, 4, 16, 5, 7, 9, *args) == -3
+
+
+def test_1d_validation(nat):
+    f = nat.lib.s6_scan_1d
+    assert f(1, 4, 16, 10, nat.VS_F32, 0, None, fake(1), None, fake(3), fake(4), fake(5),
+             None, None, 1, fake(8), None) == -1
+    assert f(1, 4, 20, 10, nat.VS_F32, 0, fake(0), fake(1), None, fake(3), fake(4), fake(5),
+             None, None, 1, fake(8), None) == -6
+
+
+def test_python_binding_checks_shapes_before_calling():
+    import torch
+    from vision_mamba_selective_amd import scan
+    u = torch.zeros(1, 4, 10)
+    with pytest.raises(ValueError):
+        scan.vim_scan_bidir(u, u, None, torch.zeros(1, 16, 9), torch.zeros(1, 16, 10),
+                            torch.zeros(2, 4, 16))
+    with pytest.raises(TypeError):
+        scan.vim_scan_bidir(u.double(), u, None, torch.zeros(1, 16, 10), torch.zeros(1, 16, 10),
+                            torch.zeros(2, 4, 16))

@@ -1,0 +1,40 @@
+"""Build libvimscan.so (HIP, gfx950) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "vimscan.hip")
+LIB = os.path.join(PKG, "libvimscan.so")
+INCLUDE = os.path.join(ROOT, "include")
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+    # packed-fp32 VALU forms are kept out of every kernel
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    return cand if os.path.exists(cand) else "hipcc"
+
+
+def build(out: str = LIB, extra=()) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building %s" % out)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build())

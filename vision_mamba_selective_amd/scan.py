@@ -1,0 +1,147 @@
+"""Torch-facing binding of the C ABI (same names as include/vimscan.h).
+
+Torch provides device memory and the stream; the functions below only check
+that tensors have the layouts the ABI expects and pass their pointers on.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _native as nat
+
+_DTYPES = {torch.float32: nat.VS_F32, torch.bfloat16: nat.VS_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _act(name, t, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _param(name, t, shape, device, optional=True):
+    if t is None:
+        if optional:
+            return
+        raise ValueError("%s is required" % name)
+    _act(name, t, shape, torch.float32, device)
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(op: int, batch: int, dim: int, seqlen: int, dtype: torch.dtype) -> int:
+    return int(nat.lib.vs_workspace_bytes(op, batch, dim, seqlen, _DTYPES[dtype]))
+
+
+def _workspace(op, batch, dim, seqlen, dtype, device, workspace):
+    need = workspace_bytes(op, batch, dim, seqlen, dtype)
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+        raise ValueError("workspace needs %d contiguous bytes" % need)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
+                   out=None, workspace=None):
+    """Vim forward + backward selective scan, merged and gated.
+
+    u, delta, z: [batch, dim, L] (fp32 or bf16; z may be None);
+    B, C: [batch, dstate, L]; A: [2, dim, dstate] fp32; Dskip, dt_bias:
+    [2, dim] fp32 or None. Returns y [batch, dim, L] in the input dtype.
+    """
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    y = torch.empty_like(u) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta), _ptr(z),
+                                _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias),
+                                int(bool(delta_softplus)), _ptr(y), _ptr(ws), ws_bytes,
+                                _stream(dev))
+    nat.check("vim_scan_bidir", rc)
+    return y
+
+
+def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
+                       delta_softplus=True, out=None, workspace=None):
+    """VMamba four-direction cross-scan of an H x W grid.
+
+    u, delta, z: [batch, dim, H*W] (row-major grid; z may be None);
+    B, C: [batch, 4, dstate, H*W] in each direction's scan order;
+    A: [4, dim, dstate]; Dskip, dt_bias: [4, dim] or None.
+    """
+    batch, dim, L = u.shape
+    if H * W != L:
+        raise ValueError("H*W must equal the token count")
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, 4, dstate, L), dt, dev)
+    _act("C", C, (batch, 4, dstate, L), dt, dev)
+    _param("A", A, (4, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (4, dim), dev)
+    _param("dt_bias", dt_bias, (4, dim), dev)
+    y = torch.empty_like(u) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    ws, ws_bytes = _workspace(nat.VS_OP_CROSS4, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vmamba_cross_scan4(batch, dim, dstate, H, W, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                    _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                    _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _ptr(ws),
+                                    ws_bytes, _stream(dev))
+    nat.check("vmamba_cross_scan4", rc)
+    return y
+
+
+def s6_scan_1d(u, delta, z, B, C, A, Dskip=None, dt_bias=None, reverse=False,
+               delta_softplus=True, out=None):
+    """One direction of the scan. A: [dim, dstate]; Dskip, dt_bias: [dim]."""
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (dim,), dev)
+    _param("dt_bias", dt_bias, (dim,), dev)
+    y = torch.empty_like(u) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    rc = nat.lib.s6_scan_1d(batch, dim, dstate, L, _DTYPES[dt], int(bool(reverse)), _ptr(u),
+                            _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                            _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _stream(dev))
+    nat.check("s6_scan_1d", rc)
+    return y
