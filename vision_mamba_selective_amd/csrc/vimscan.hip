@@ -74,62 +74,100 @@ __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
+// Raw loads keep the loaded bits untouched so that the conversion (and the
+// wait for the load) happens where the value is used, not where it is loaded.
+__device__ __forceinline__ uint32_t ld_raw(const float* p, int64_t i) { return __float_as_uint(p[i]); }
+__device__ __forceinline__ uint32_t ld_raw(const uint16_t* p, int64_t i) { return p[i]; }
+template <typename T>
+__device__ __forceinline__ float from_raw(uint32_t r) {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(r << 16);
+    else return __uint_as_float(r);
+}
 __device__ __forceinline__ void st(float* p, int64_t i, float v) { p[i] = v; }
-// fp32 -> bf16, round to nearest, ties to even (NaN stays NaN).
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ void st(uint16_t* p, int64_t i, float v) {
-    uint32_t x = __float_as_uint(v);
-    uint32_t r = (x & 0x7fffffffu) > 0x7f800000u ? (x | 0x00400000u)
-                                                  : x + 0x7fffu + ((x >> 16) & 1u);
-    p[i] = static_cast<uint16_t>(r >> 16);
+    p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
 
 // ------------------------------------------------------------- lane moves
+// DPP move whose result feeds a VALU op; the compiler folds it into the
+// consumer (v_mul_f32_dpp etc.) when both operands are VGPRs.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
-                                                      0xf, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 // value of lane I of this 16-lane row, in every lane of the row (row_newbcast)
 template <int I>
 __device__ __forceinline__ float row_bcast(float v) { return dpp<0x150 + I>(v); }
 
-// value of lane (lane ^ M) within the row
-template <int M>
-__device__ __forceinline__ float xor_lane(float v) {
-    if constexpr (M == 8) return dpp<0x128>(v);                 // row_ror:8
-    else if constexpr (M == 2) return dpp<0x4e>(v);             // quad_perm [2,3,0,1]
-    else if constexpr (M == 1) return dpp<0xb1>(v);             // quad_perm [1,0,3,2]
-    else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101f));  // xor 4
-}
-
-// Transpose-reduce 16 values per lane across the 16 lanes of a row:
-// on return c[0] of lane j holds sum over the row's lanes of c[j].
-template <int M, int V>
-__device__ __forceinline__ void reduce_stage(float (&c)[16], int lane) {
-    const bool hi = (lane & M) != 0;
-#pragma unroll
-    for (int k = 0; k < V / 2; ++k) {
-        const float lo_v = c[k], hi_v = c[k + V / 2];
-        const float send = hi ? lo_v : hi_v;
-        const float keep = hi ? hi_v : lo_v;
-        c[k] = keep + xor_lane<M>(send);
-    }
-}
-__device__ __forceinline__ float row_transpose_sum(float (&c)[16], int lane) {
-    reduce_stage<8, 16>(c, lane);
-    reduce_stage<4, 8>(c, lane);
-    reduce_stage<2, 4>(c, lane);
-    reduce_stage<1, 2>(c, lane);
-    return c[0];
+// Transpose-reduce across the 16 lanes of a row: lane n holds c[i] = its
+// state's share of token i's read-out; on return lane j holds the sum over
+// the row's lanes of c[j]. Each halving stage pairs lane j with lane j^m. The
+// two cross-bank stages (m = 8, 4) write the kept half of each bank (4-lane
+// group) with bank-masked DPP adds, 2 per pair, in one asm block: its
+// leading s_nop gives the two wait states a DPP read needs after the VALU
+// write of its source, and inside the block every DPP source was written at
+// least 7 instructions earlier; the trailing s_nop covers the DPP reads that
+// follow the block. The in-bank stages (m = 2, 1) add both halves and select.
+#define VS_ADD8(T, C, K) \
+    "v_add_f32_dpp %[" #T "], %[" #C "], %[" #C "] row_ror:8 row_mask:0xf bank_mask:" K "\n\t"
+#define VS_ADD4(V, T, R, K) \
+    "v_add_f32_dpp %[" #V "], %[" #T "], %[" #T "] " R " row_mask:0xf bank_mask:" K "\n\t"
+__device__ __forceinline__ float row_transpose_sum(const float (&c)[16], int lane) {
+    float t0, t1, t2, t3, t4, t5, t6, t7, v0, v1, v2, v3;
+    asm("s_nop 1\n\t"
+        VS_ADD8(t0, c0, "0x3") VS_ADD8(t0, c8, "0xc")
+        VS_ADD8(t1, c1, "0x3") VS_ADD8(t1, c9, "0xc")
+        VS_ADD8(t2, c2, "0x3") VS_ADD8(t2, c10, "0xc")
+        VS_ADD8(t3, c3, "0x3") VS_ADD8(t3, c11, "0xc")
+        VS_ADD8(t4, c4, "0x3") VS_ADD8(t4, c12, "0xc")
+        VS_ADD8(t5, c5, "0x3") VS_ADD8(t5, c13, "0xc")
+        VS_ADD8(t6, c6, "0x3") VS_ADD8(t6, c14, "0xc")
+        VS_ADD8(t7, c7, "0x3") VS_ADD8(t7, c15, "0xc")
+        VS_ADD4(v0, t0, "row_ror:12", "0x5") VS_ADD4(v0, t4, "row_ror:4", "0xa")
+        VS_ADD4(v1, t1, "row_ror:12", "0x5") VS_ADD4(v1, t5, "row_ror:4", "0xa")
+        VS_ADD4(v2, t2, "row_ror:12", "0x5") VS_ADD4(v2, t6, "row_ror:4", "0xa")
+        VS_ADD4(v3, t3, "row_ror:12", "0x5") VS_ADD4(v3, t7, "row_ror:4", "0xa")
+        "s_nop 1"
+        : [t0] "=&v"(t0), [t1] "=&v"(t1), [t2] "=&v"(t2), [t3] "=&v"(t3), [t4] "=&v"(t4),
+          [t5] "=&v"(t5), [t6] "=&v"(t6), [t7] "=&v"(t7), [v0] "=&v"(v0), [v1] "=&v"(v1),
+          [v2] "=&v"(v2), [v3] "=&v"(v3)
+        : [c0] "v"(c[0]), [c1] "v"(c[1]), [c2] "v"(c[2]), [c3] "v"(c[3]), [c4] "v"(c[4]),
+          [c5] "v"(c[5]), [c6] "v"(c[6]), [c7] "v"(c[7]), [c8] "v"(c[8]), [c9] "v"(c[9]),
+          [c10] "v"(c[10]), [c11] "v"(c[11]), [c12] "v"(c[12]), [c13] "v"(c[13]),
+          [c14] "v"(c[14]), [c15] "v"(c[15]));
+    const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+    const float s0 = v0 + dpp<0x4e>(v0), s2 = v2 + dpp<0x4e>(v2);   // quad_perm [2,3,0,1]
+    const float s1 = v1 + dpp<0x4e>(v1), s3 = v3 + dpp<0x4e>(v3);
+    const float w0 = b1 ? s2 : s0, w1 = b1 ? s3 : s1;
+    const float r0 = w0 + dpp<0xb1>(w0), r1 = w1 + dpp<0xb1>(w1);   // quad_perm [1,0,3,2]
+    return b0 ? r1 : r0;
 }
 
 // ---------------------------------------------------------------- math
-// softplus(x) = log(1 + e^x) in the form that keeps the small result for
-// negative x and does not overflow for large x.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// softplus(x) = max(x, 0) + log1p(w), w = e^{-|x|} in (0, 1].
+// log1p(w) = 2 atanh(r) with r = w / (2 + w) in (0, 1/3], summed as the odd
+// series 2 (r + r^3/3 + ... + r^13/13); the first omitted term is below
+// 2e-8 of the result, so the value is as accurate as the fp32 exp and rcp.
 __device__ __forceinline__ float softplus_f(float x) {
-    return x > 0.f ? x + log1pf(expf(-x)) : log1pf(expf(x));
+    const float w = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+    const float r = w * __builtin_amdgcn_rcpf(2.f + w);
+    const float q = r * r;
+    float p = 1.f / 13.f;
+    p = fmaf(p, q, 1.f / 11.f);
+    p = fmaf(p, q, 1.f / 9.f);
+    p = fmaf(p, q, 1.f / 7.f);
+    p = fmaf(p, q, 1.f / 5.f);
+    p = fmaf(p, q, 1.f / 3.f);
+    p = fmaf(p, q, 1.f);
+    return fmaxf(x, 0.f) + 2.f * r * p;
 }
-__device__ __forceinline__ float silu_f(float z) { return z / (1.f + expf(-z)); }
+// silu(z) = z * sigmoid(z) = z / (1 + e^{-z})
+__device__ __forceinline__ float silu_f(float z) {
+    return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
 
 __device__ __forceinline__ int64_t visit(int order, int64_t t, int64_t L, int H, int W) {
     switch (order) {
@@ -157,16 +195,27 @@ struct Unroll<0> {
 // ---------------------------------------------------------------- kernel
 // Workgroup = 4 waves = 16 rows. Row roles per mode:
 //   1-D   : 16 channels, one direction (args.reverse)
-//   Vim   : 8 channels x {forward, backward}
-//   Cross4: 4 channels x {row-major, reverse, column-major, reverse}
-template <typename T, int MODE>
+//   Vim   : 8 channels x {forward, backward}; rows 2c and 2c+1 of channel c
+//
+// Loop over blocks of 16 tokens. Global loads run two blocks ahead (raw
+// bits in registers), the B/C tile of the next block is written to the other
+// LDS buffer at the end of each step, and the per-step barrier orders LDS
+// only. For the Vim merge every block step is one of three phases:
+//   steps < F : every token of the step is the first of its two visits
+//               (forward token t < L/2, backward token > L/2): store y_k as
+//               an fp32 partial sum;
+//   step F    : the steps share tokens: forward stores, a fence, and the
+//               backward row finishes the shared ones;
+//   steps > F : every token is the second visit: add the partial sum
+//               (prefetched one step ahead), gate, store y.
+// with F = (L-1) / 32. The only global-memory fence is in step F; partial
+// sums are read only after it.
+template <typename T, int MODE, bool GATE, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
-    constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
+    constexpr int kDirs = MODE == kModeVim ? 2 : 1;
     constexpr int kChPerWg = 16 / kDirs;
-    // B/C tiles: 1-D and Vim share B, C over directions (one tile per distinct
-    // token order); Cross4 has per-direction B, C in scan order.
-    constexpr int kSides = MODE == kMode1D ? 1 : (MODE == kModeVim ? 2 : 4);
-    __shared__ float tile[2][kSides][2][kRowLanes][kTilePad];
+    constexpr int kSides = kDirs;              // one B/C tile per token order
+    __shared__ __attribute__((aligned(16))) float tile[2][kSides][2][kRowLanes][kTilePad];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -175,151 +224,170 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const int dir = row_in_wg % kDirs;
     const int ch = row_in_wg / kDirs;
     const int64_t b = blockIdx.y;
-    const int64_t d = static_cast<int64_t>(blockIdx.x) * kChPerWg + ch;
-    const bool active = d < a.dim;
-    const int64_t L = a.L;
-    const T* __restrict__ u = static_cast<const T*>(a.u);
-    const T* __restrict__ dl = static_cast<const T*>(a.delta);
-    const T* __restrict__ z = static_cast<const T*>(a.z);
-    const T* __restrict__ Bp = static_cast<const T*>(a.B);
-    const T* __restrict__ Cp = static_cast<const T*>(a.C);
-    T* __restrict__ y = static_cast<T*>(a.y);
-
-    int order;
-    if (MODE == kModeVim) order = dir;                 // 0 forward, 1 backward
-    else if (MODE == kModeCross4) order = dir;         // 0..3
-    else order = a.reverse ? kRev : kFwd;
+    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChPerWg + ch;
+    const bool active = d0 < a.dim;
+    const int64_t d = active ? d0 : 0;
+    const int L = static_cast<int>(a.L);
+    const int nblk = a.nblk;
+    const bool rev = MODE == kModeVim ? dir == 1 : a.reverse != 0;
 
     // per-row parameters
-    const int pdir = MODE == kMode1D ? 0 : dir;
-    const int64_t prow = static_cast<int64_t>(pdir) * a.dim + (active ? d : 0);
-    const float kLog2e = 1.4426950408889634f;
+    const int64_t prow = (MODE == kModeVim ? dir * a.dim : 0) + d;
     const float A2 = (active && n < a.dstate) ? a.A[prow * a.dstate + n] * kLog2e : 0.f;
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
-    const int64_t rowbase = (b * a.dim + (active ? d : 0)) * L;
+    const int64_t rowbase = (b * a.dim + d) * a.L;
+    const T* __restrict__ u_row = static_cast<const T*>(a.u) + rowbase;
+    const T* __restrict__ dl_row = static_cast<const T*>(a.delta) + rowbase;
+    const T* __restrict__ z_row = GATE ? static_cast<const T*>(a.z) + rowbase : nullptr;
+    T* __restrict__ y_row = static_cast<T*>(a.y) + rowbase;
+    float* __restrict__ part_row = a.partial + rowbase;
 
-    // ---- B/C tile staging: element e -> (side, which, state, slot)
-    constexpr int kTileElems = kSides * 2 * kRowLanes * kBlockTok;
-    constexpr int kPerThread = (kTileElems + kThreads - 1) / kThreads;
-    auto tile_src = [&](int e, int blk, float& v) {
-        const int slot = e & 15, st_n = (e >> 4) & 15, which = (e >> 8) & 1, side = e >> 9;
-        const int64_t t = static_cast<int64_t>(blk) * kBlockTok + slot;
-        v = 0.f;
-        if (t < L && st_n < a.dstate) {
-            const T* src = which ? Cp : Bp;
-            int64_t idx;
-            if (MODE == kModeCross4) {
-                idx = ((b * 4 + side) * a.dstate + st_n) * L + t;       // scan order
-            } else {
-                const int sorder = MODE == kModeVim ? side : order;
-                const int64_t p = sorder == kRev ? L - 1 - t : t;
-                idx = (b * a.dstate + st_n) * L + p;
-            }
-            v = ld(src, idx);
-        }
-    };
-    float stage[kPerThread];
-    auto stage_load = [&](int blk) {
+    // ---- B/C staging: thread (sn = tid/16, slot = tid%16) copies entry
+    // (state sn, token slot) of every (side, B|C) tile. Rows of states >=
+    // dstate stay zero (written once), so those state lanes never change.
+    constexpr int kStage = kSides * 2;
+    const int sn = tid >> 4, slot = tid & 15;
+    const bool sn_ok = sn < a.dstate;
+    const int64_t bc_row = (b * a.dstate + (sn_ok ? sn : 0)) * a.L;
+    const T* __restrict__ Bsrc = static_cast<const T*>(a.B) + bc_row;
+    const T* __restrict__ Csrc = static_cast<const T*>(a.C) + bc_row;
+    auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
+        const int t = blk * kBlockTok + slot;
+        const int tc = t < L ? t : L - 1;     // padding slots: any valid entry
 #pragma unroll
-        for (int r = 0; r < kPerThread; ++r) {
-            const int e = tid + r * kThreads;
-            stage[r] = 0.f;
-            if (e < kTileElems) tile_src(e, blk, stage[r]);
+        for (int r = 0; r < kStage; ++r) {
+            const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
+            sr[r] = ld_raw((r & 1) ? Csrc : Bsrc, side_rev ? L - 1 - tc : tc);
         }
     };
-    auto stage_store = [&](int buf) {
+    // threads of states >= dstate write their (unused) values into the
+    // padding column 16 of their tile row, so the store needs no branch
+    const int st_col = sn_ok ? slot : kRowLanes;
+    auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) {
 #pragma unroll
-        for (int r = 0; r < kPerThread; ++r) {
-            const int e = tid + r * kThreads;
-            if (e < kTileElems) {
-                const int slot = e & 15, st_n = (e >> 4) & 15, which = (e >> 8) & 1, side = e >> 9;
-                tile[buf][side][which][st_n][slot] = stage[r];
-            }
+        for (int r = 0; r < kStage; ++r)
+            tile[buf][r >> 1][r & 1][sn][st_col] = from_raw<T>(sr[r]);
+    };
+    if (!sn_ok) {
+#pragma unroll
+        for (int r = 0; r < kStage; ++r) {
+            tile[0][r >> 1][r & 1][sn][slot] = 0.f;
+            tile[1][r >> 1][r & 1][sn][slot] = 0.f;
         }
+    }
+
+    // ---- this lane's token of a block (slot n); unconditional loads on a
+    // clamped index so that they can all be in flight together.
+    const int Fstep = MODE == kModeVim ? (L - 1) / (2 * kBlockTok) : -1;
+    struct Tok { uint32_t u, dl, z; };
+    auto tok_pos = [&](int blk) {
+        const int t = blk * kBlockTok + n;
+        const int tc = t < L ? t : L - 1;
+        return rev ? L - 1 - tc : tc;
+    };
+    auto tok_load = [&](int blk, Tok& k) {
+        const int p = tok_pos(blk);
+        k.u = ld_raw(u_row, p);
+        k.dl = ld_raw(dl_row, p);
+        // z is needed only by the visit that finishes the token; other
+        // blocks load entry 0 of the row (one cached line) instead of
+        // branching, which would stall on the in-flight registers
+        if (GATE) k.z = ld_raw(z_row, (MODE != kModeVim || blk >= Fstep) ? p : 0);
     };
 
-    // ---- per-lane token data for a block: token p of slot n (= lane in row)
-    struct Tok { float u, dl, z; int64_t p; bool ok; };
-    auto tok_load = [&](int blk) {
-        Tok k;
-        const int64_t t = static_cast<int64_t>(blk) * kBlockTok + n;
-        k.ok = active && t < L;
-        k.p = k.ok ? visit(order, t, L, a.H, a.W) : 0;
-        k.u = k.ok ? ld(u, rowbase + k.p) : 0.f;
-        k.dl = k.ok ? ld(dl, rowbase + k.p) : 0.f;
-        k.z = (k.ok && z) ? ld(z, rowbase + k.p) : 0.f;
-        return k;
-    };
-
-    stage_load(0);
-    stage_store(0);
-    Tok cur = tok_load(0);
-    __syncthreads();
+    uint32_t sr[kStage];
+    stage_load(0, sr);
+    stage_store(0, sr);
+    Tok tA{}, tB{};
+    tok_load(0, tA);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     float h = 0.f;
-    for (int blk = 0; blk < a.nblk; ++blk) {
+    // One block step. `cur` holds this block's token data (loaded one step
+    // earlier), `nxt` receives the next block's; the loop below alternates
+    // the two so that no register of an in-flight load is ever copied.
+    auto step = [&](const int blk, Tok& cur, Tok& nxt) {
         const int buf = blk & 1;
-        const bool more = blk + 1 < a.nblk;
-        if (more) stage_load(blk + 1);
-        Tok nxt{};
-        if (more) nxt = tok_load(blk + 1);
+        const int p = tok_pos(blk);
+        const bool ok = active && blk * kBlockTok + n < L;
+        // the other direction's partial sum, for blocks after step F (it was
+        // stored at step F or earlier, before F's fence); earlier blocks load
+        // entry 0 of the row instead (unused) rather than branch. Issued
+        // before the prefetch so that waiting for it does not wait for those.
+        float part = 0.f;
+        if (MODE == kModeVim)
+            part = __hip_atomic_load(&part_row[blk > Fstep ? p : 0], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        // prefetch the next block; on the last step this reloads the last
+        // block (unused), which keeps the loads free of branches
+        const int nb = blk + 1 < nblk ? blk + 1 : blk;
+        stage_load(nb, sr);
+        tok_load(nb, nxt);
 
-        // delta and delta*u of this lane's token (zero for padding slots, so
-        // they leave the state unchanged: exp(0) = 1, no input)
-        float dlt = 0.f, du = 0.f;
-        if (cur.ok) {
-            const float x = cur.dl + bias;
-            dlt = a.softplus ? softplus_f(x) : x;
-            du = dlt * cur.u;
+        // delta and delta*u of this lane's token (zero in padding slots, which
+        // then leave the state unchanged: exp(0) = 1 and no input)
+        const float cu = from_raw<T>(cur.u);
+        const float x = from_raw<T>(cur.dl) + bias;
+        const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
+        const float du = dlt * cu;
+
+        const int side = MODE == kModeVim ? dir : 0;
+        const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][side][0][n][0]);
+        const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][side][1][n][0]);
+        float Bv[16], Cv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 bb = Bt[q], cc = Ct[q];
+            Bv[4 * q] = bb.x; Bv[4 * q + 1] = bb.y; Bv[4 * q + 2] = bb.z; Bv[4 * q + 3] = bb.w;
+            Cv[4 * q] = cc.x; Cv[4 * q + 1] = cc.y; Cv[4 * q + 2] = cc.z; Cv[4 * q + 3] = cc.w;
         }
-        const int side = MODE == kMode1D ? 0 : dir;
-        const float* Bt = &tile[buf][side][0][n][0];
-        const float* Ct = &tile[buf][side][1][n][0];
         float c[16];
         Unroll<16>::run([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             const float e = __builtin_amdgcn_exp2f(row_bcast<i>(dlt) * A2);
-            h = fmaf(e, h, row_bcast<i>(du) * Bt[i]);
-            c[i] = Ct[i] * h;
+            h = fmaf(e, h, row_bcast<i>(du) * Bv[i]);
+            c[i] = Cv[i] * h;
         });
-        const float yk = row_transpose_sum(c, lane) + Dk * cur.u;
+        const float yk = fmaf(Dk, cu, row_transpose_sum(c, lane));
+        const float gate = GATE ? silu_f(from_raw<T>(cur.z)) : 1.f;
 
-        // ---- merge and store (lane n holds token slot n)
         if (MODE == kMode1D) {
-            if (cur.ok) {
-                float v = yk;
-                if (z) v *= silu_f(cur.z);
-                st(y, rowbase + cur.p, v);
-            }
-        } else if (MODE == kModeVim) {
-            // This lane's scan step is t; the other direction visits the same
-            // token at step L-1-t. The direction whose block finishes the
-            // token first stores a partial sum; on a tie (both in this block
-            // step) the forward row stores and the backward row finishes.
-            const int64_t t_self = static_cast<int64_t>(blk) * kBlockTok + n;
-            const int64_t blk_other = (L - 1 - t_self) / kBlockTok;
+            if (ok) st(y_row, p, yk * gate);
+        } else if (blk < Fstep) {
+            if (ok) part_row[p] = yk;
+        } else if (blk > Fstep) {
+            if (ok) st(y_row, p, (yk + part) * gate);
+        } else {
+            // step F: tokens finished by the other direction in an earlier
+            // step, or (forward row) shared with the backward row in this one
+            const int t_self = blk * kBlockTok + n;
+            const int blk_other = (L - 1 - t_self) / kBlockTok;
             const bool first = blk < blk_other || (blk == blk_other && dir == 0);
-            if (cur.ok && first)
-                __hip_atomic_store(&a.partial[rowbase + cur.p], yk, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            // block steps whose forward and backward blocks share tokens
-            const int64_t b32 = static_cast<int64_t>(blk) * 2 * kBlockTok;
-            if (L - 2 * kBlockTok + 1 <= b32 && b32 <= L - 1)
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-            if (cur.ok && !first) {
-                const float other = __hip_atomic_load(&a.partial[rowbase + cur.p],
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                float v = yk + other;
-                if (z) v *= silu_f(cur.z);
-                st(y, rowbase + cur.p, v);
+            if (ok && first)
+                __hip_atomic_store(&part_row[p], yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            if (ok && !first) {
+                const float other = __hip_atomic_load(&part_row[p], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+                st(y_row, p, (yk + other) * gate);
             }
         }
 
-        if (more) stage_store(buf ^ 1);
-        __syncthreads();
-        if (more) cur = nxt;
+        stage_store(buf ^ 1, sr);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    int blk = 0;
+    for (; blk + 1 < nblk; blk += 2) {
+        step(blk, tA, tB);
+        step(blk + 1, tB, tA);
     }
+    if (blk < nblk) step(blk, tA, tB);
 }
 
 // ---------------------------------------------------------------- host side
@@ -413,11 +481,19 @@ int launch_t(const Call& c) {
     a.softplus = c.softplus ? 1 : 0;
     a.reverse = c.reverse ? 1 : 0;
     a.nblk = static_cast<int>((c.L + kBlockTok - 1) / kBlockTok);
-    constexpr int kChPerWg = MODE == kModeVim ? 8 : (MODE == kModeCross4 ? 4 : 16);
+    constexpr int kChPerWg = MODE == kModeVim ? 8 : 16;
     dim3 grid(static_cast<unsigned>((c.dim + kChPerWg - 1) / kChPerWg),
               static_cast<unsigned>(c.batch));
-    hipLaunchKernelGGL((rowscan_kernel<T, MODE>), grid, dim3(kThreads), 0,
-                       static_cast<hipStream_t>(c.stream), a);
+    hipStream_t st = static_cast<hipStream_t>(c.stream);
+    const dim3 blk(kThreads);
+    if (c.z && c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, true>), grid, blk, 0, st, a);
+    else if (c.z)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, false>), grid, blk, 0, st, a);
+    else if (c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, true>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, false>), grid, blk, 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return VS_OK;
