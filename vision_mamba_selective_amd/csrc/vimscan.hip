@@ -236,12 +236,25 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const float A2 = (active && n < a.dstate) ? a.A[prow * a.dstate + n] * kLog2e : 0.f;
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
-    const int64_t rowbase = (b * a.dim + d) * a.L;
-    const T* __restrict__ u_row = static_cast<const T*>(a.u) + rowbase;
-    const T* __restrict__ dl_row = static_cast<const T*>(a.delta) + rowbase;
-    const T* __restrict__ z_row = GATE ? static_cast<const T*>(a.z) + rowbase : nullptr;
-    T* __restrict__ y_row = static_cast<T*>(a.y) + rowbase;
-    float* __restrict__ part_row = a.partial + rowbase;
+    // Every tensor is addressed as its scalar base address plus a 32-bit
+    // byte offset (tensors stay below 4 GiB), which keeps per-lane 64-bit
+    // address arithmetic out of the loop.
+    constexpr uint32_t kEs = sizeof(T);
+    const uint32_t rowoff = static_cast<uint32_t>((b * a.dim + d) * a.L);
+    const char* __restrict__ ub = static_cast<const char*>(a.u);
+    const char* __restrict__ db = static_cast<const char*>(a.delta);
+    const char* __restrict__ zb = static_cast<const char*>(a.z);
+    char* __restrict__ yb = static_cast<char*>(a.y);
+    char* __restrict__ pb = reinterpret_cast<char*>(a.partial);
+    auto act_at = [&](const char* base, int p) {
+        return ld_raw(reinterpret_cast<const T*>(base + (rowoff + static_cast<uint32_t>(p)) * kEs), 0);
+    };
+    auto part_at = [&](int p) {
+        return reinterpret_cast<float*>(pb + (rowoff + static_cast<uint32_t>(p)) * 4u);
+    };
+    auto y_at = [&](int p) {
+        return reinterpret_cast<T*>(yb + (rowoff + static_cast<uint32_t>(p)) * kEs);
+    };
 
     // ---- B/C staging: thread (sn = tid/16, slot = tid%16) copies entry
     // (state sn, token slot) of every (side, B|C) tile. Rows of states >=
@@ -249,16 +262,17 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     constexpr int kStage = kSides * 2;
     const int sn = tid >> 4, slot = tid & 15;
     const bool sn_ok = sn < a.dstate;
-    const int64_t bc_row = (b * a.dstate + (sn_ok ? sn : 0)) * a.L;
-    const T* __restrict__ Bsrc = static_cast<const T*>(a.B) + bc_row;
-    const T* __restrict__ Csrc = static_cast<const T*>(a.C) + bc_row;
+    const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
+    const char* __restrict__ Bb = static_cast<const char*>(a.B);
+    const char* __restrict__ Cb = static_cast<const char*>(a.C);
     auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
         const int t = blk * kBlockTok + slot;
         const int tc = t < L ? t : L - 1;     // padding slots: any valid entry
 #pragma unroll
         for (int r = 0; r < kStage; ++r) {
             const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
-            sr[r] = ld_raw((r & 1) ? Csrc : Bsrc, side_rev ? L - 1 - tc : tc);
+            const uint32_t off = (bc_row + static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
+            sr[r] = ld_raw(reinterpret_cast<const T*>(((r & 1) ? Cb : Bb) + off), 0);
         }
     };
     // threads of states >= dstate write their (unused) values into the
@@ -288,12 +302,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     };
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
-        k.u = ld_raw(u_row, p);
-        k.dl = ld_raw(dl_row, p);
+        k.u = act_at(ub, p);
+        k.dl = act_at(db, p);
         // z is needed only by the visit that finishes the token; other
         // blocks load entry 0 of the row (one cached line) instead of
         // branching, which would stall on the in-flight registers
-        if (GATE) k.z = ld_raw(z_row, (MODE != kModeVim || blk >= Fstep) ? p : 0);
+        if (GATE) k.z = act_at(zb, (MODE != kModeVim || blk >= Fstep) ? p : 0);
     };
 
     uint32_t sr[kStage];
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // before the prefetch so that waiting for it does not wait for those.
         float part = 0.f;
         if (MODE == kModeVim)
-            part = __hip_atomic_load(&part_row[blk > Fstep ? p : 0], __ATOMIC_RELAXED,
+            part = __hip_atomic_load(part_at(blk > Fstep ? p : 0), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
         // prefetch the next block; on the last step this reloads the last
         // block (unused), which keeps the loads free of branches
@@ -355,11 +369,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const float gate = GATE ? silu_f(from_raw<T>(cur.z)) : 1.f;
 
         if (MODE == kMode1D) {
-            if (ok) st(y_row, p, yk * gate);
+            if (ok) st(y_at(p), 0, yk * gate);
         } else if (blk < Fstep) {
-            if (ok) part_row[p] = yk;
+            if (ok) *part_at(p) = yk;
         } else if (blk > Fstep) {
-            if (ok) st(y_row, p, (yk + part) * gate);
+            if (ok) st(y_at(p), 0, (yk + part) * gate);
         } else {
             // step F: tokens finished by the other direction in an earlier
             // step, or (forward row) shared with the backward row in this one
@@ -367,12 +381,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const int blk_other = (L - 1 - t_self) / kBlockTok;
             const bool first = blk < blk_other || (blk == blk_other && dir == 0);
             if (ok && first)
-                __hip_atomic_store(&part_row[p], yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(part_at(p), yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
             if (ok && !first) {
-                const float other = __hip_atomic_load(&part_row[p], __ATOMIC_RELAXED,
+                const float other = __hip_atomic_load(part_at(p), __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-                st(y_row, p, (yk + other) * gate);
+                st(y_at(p), 0, (yk + other) * gate);
             }
         }
 
@@ -433,7 +447,10 @@ int validate(const Call& c) {
     if (c.L > (int64_t(1) << 30) || c.dim > (int64_t(1) << 30))
         return fail(VS_ERR_SHAPE, "sequence length or dim too large");
     const int64_t elems = c.batch * c.dim * c.L;
-    if (elems > (int64_t(1) << 40)) return fail(VS_ERR_SHAPE, "problem too large");
+    // kernels address every tensor with 32-bit byte offsets (fp32 partial
+    // sums included), so each tensor must stay below 4 GiB
+    if (elems >= (int64_t(1) << 30) || c.batch * 4 * c.dstate * c.L >= (int64_t(1) << 30))
+        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
     if (!c.u || !c.delta || !c.B || !c.C || !c.A || !c.y)
         return fail(VS_ERR_NULL, "u, delta, B, C, A and y must not be NULL");
     const size_t es = c.dtype == VS_BF16 ? 2 : 4;
