@@ -79,9 +79,13 @@ enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2 };
 /* Largest supported state size (the pages use 16 by default and 8 in a test). */
 #define VS_MAX_DSTATE 16
 
-/* Bytes of device workspace an operation needs for its direction merge:
- * one fp32 partial sum per output element when y is bf16, 0 otherwise (an
- * fp32 y holds the partial sums itself). Returns 0 for invalid arguments. */
+/* Bytes of device workspace an operation needs, in units of E =
+ * batch*dim*seqlen elements. Direction merge: fp32 buffers of E floats,
+ * one for VS_OP_VIM_BIDIR and two for VS_OP_CROSS4 (one per pair of opposite
+ * directions); an fp32 y serves as the first, so fp32 needs one fewer.
+ * VS_OP_CROSS4 also holds column-major copies of u and delta (2 E elements
+ * of the input dtype). VS_OP_1D needs none. Returns 0 for invalid
+ * arguments. */
 size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);
 
 /*
@@ -116,7 +120,10 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
  *   B, C           [batch][4][dstate][L]: direction k's B_t, C_t stored in
  *                  its own scan order (entry t is used at scan step t)
  *   A              [4][dim][dstate]; Dskip, dt_bias [4][dim] or NULL
- *   workspace      at least vs_workspace_bytes(VS_OP_CROSS4, ...) bytes
+ *   delta_softplus as for vim_scan_bidir; delta_raw is shared by the four
+ *                  directions (spatial order), dt_bias is per direction
+ *   workspace      at least vs_workspace_bytes(VS_OP_CROSS4, ...) bytes;
+ *                  contents on entry are ignored, on return unspecified
  */
 int vmamba_cross_scan4(int64_t batch, int64_t dim, int64_t dstate, int64_t H, int64_t W,
                        int dtype, const void* u, const void* delta, const void* z,

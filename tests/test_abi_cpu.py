@@ -49,8 +49,12 @@ def test_version_and_strerror(nat):
 def test_workspace_bytes(nat):
     f = nat.lib.vs_workspace_bytes
     assert f(0, 8, 768, 4097, nat.VS_BF16) == 8 * 768 * 4097 * 4
-    assert f(1, 8, 384, 4096, nat.VS_BF16) == 8 * 384 * 4096 * 4
+    e = 8 * 384 * 4096
+    assert f(1, 8, 384, 4096, nat.VS_BF16) == 2 * e * 4 + 2 * e * 2   # 2 merge buffers, u^T, delta^T
+    assert f(1, 8, 384, 4096, nat.VS_F32) == e * 4 + 2 * e * 4        # y is the first buffer
     assert f(0, 8, 768, 4097, nat.VS_F32) == 0          # fp32 y holds the partial sums
+    assert f(2, 8, 768, 4097, nat.VS_F32) == 0
+    assert f(0, 8, 768, 4097, 5) == 0
     assert f(2, 8, 768, 4097, nat.VS_BF16) == 0
     assert f(0, 0, 768, 4097, nat.VS_BF16) == 0
 
@@ -109,6 +113,10 @@ def test_cross4_validation(nat):
     assert f(1, 4, 16, 5, -1, nat.VS_F32, *args) == -2
     assert f(1, 4, 32, 5, 7, nat.VS_F32, *args) == -6
     assert f(1, 4, 16, 5, 7, 9, *args) == -3
+    # the cross-scan needs a workspace even for fp32 (its second merge buffer)
+    no_ws = args[:10] + [None, 0, None]
+    assert f(1, 4, 16, 5, 7, nat.VS_F32, *no_ws) == -8
+    assert f(1, 4, 16, 1 << 21, 7, nat.VS_F32, *args) == -2
 
 
 def test_1d_validation(nat):

@@ -44,9 +44,10 @@ constexpr int kRowLanes = 16;       // one recurrence per DPP row
 constexpr int kBlockTok = 16;       // tokens per block step
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kTilePad = 20;        // LDS row stride (floats) of a 16-token tile
+constexpr int kTr = 32;             // grid transpose tile edge
+constexpr int kTrPad = kTr + 1;
 
 enum Mode { kMode1D = 0, kModeVim = 1, kModeCross4 = 2 };
-enum Order { kFwd = 0, kRev = 1, kCol = 2, kColRev = 3 };
 
 struct ScanArgs {
     const void* u;
@@ -59,6 +60,9 @@ struct ScanArgs {
     const float* dt_bias;
     void* y;
     float* partial;     // fp32 partial sums for the merge ([batch][dim][L])
+    float* partial2;    // cross-scan: the column-major pair's partial sums
+    const void* uT;     // cross-scan: u and delta transposed to column-major
+    const void* deltaT;
     int64_t dim;
     int64_t L;
     int H;
@@ -169,15 +173,6 @@ __device__ __forceinline__ float silu_f(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
-__device__ __forceinline__ int64_t visit(int order, int64_t t, int64_t L, int H, int W) {
-    switch (order) {
-    case kFwd: return t;
-    case kRev: return L - 1 - t;
-    case kCol: return (t % H) * W + t / H;
-    default: { int64_t r = L - 1 - t; return (r % H) * W + r / H; }
-    }
-}
-
 template <int I>
 struct Unroll {
     template <typename F>
@@ -194,45 +189,69 @@ struct Unroll<0> {
 
 // ---------------------------------------------------------------- kernel
 // Workgroup = 4 waves = 16 rows. Row roles per mode:
-//   1-D   : 16 channels, one direction (args.reverse)
-//   Vim   : 8 channels x {forward, backward}; rows 2c and 2c+1 of channel c
+//   1-D     : 16 channels, one direction (args.reverse)
+//   Vim     : 8 channels x {forward, backward}; rows 2c and 2c+1 of channel c
+//   cross-4 : 4 channels x the four VMamba orders. Waves 0-1 hold the
+//             row-major pairs (k = 0 forward, 1 reverse) of channels 0-1 and
+//             2-3, waves 2-3 the column-major pairs (k = 2, 3); within a
+//             wave rows 2c' and 2c'+1 are one channel's pair.
+// A direction and its reverse form a pair that visits every token at scan
+// steps t and L-1-t; the two rows of a pair share one wave. The column-major
+// pair reads u and delta from copies transposed to column-major order (a
+// pre-pass), so its token at step t is entry t (or L-1-t) of the copy, read
+// as contiguously as the row-major pair's; its partial sums stay in that
+// order and are transposed back when the workgroup merges the pairs.
 //
 // Loop over blocks of 16 tokens. Global loads run two blocks ahead (raw
 // bits in registers), the B/C tile of the next block is written to the other
 // LDS buffer at the end of each step, and the per-step barrier orders LDS
-// only. For the Vim merge every block step is one of three phases:
+// only. For the pair merge every block step is one of three phases:
 //   steps < F : every token of the step is the first of its two visits
 //               (forward token t < L/2, backward token > L/2): store y_k as
 //               an fp32 partial sum;
 //   step F    : the steps share tokens: forward stores, a fence, and the
 //               backward row finishes the shared ones;
 //   steps > F : every token is the second visit: add the partial sum
-//               (prefetched one step ahead), gate, store y.
+//               (prefetched one step ahead) and finish the token,
 // with F = (L-1) / 32. The only global-memory fence is in step F; partial
-// sums are read only after it.
+// sums are read only after it. Vim finishes a token by gating and storing
+// y; the cross-scan stores the pair's sum, and after the loop the workgroup
+// adds its two pairs' sums, gates and stores y.
 template <typename T, int MODE, bool GATE, bool SOFTPLUS>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
-    constexpr int kDirs = MODE == kModeVim ? 2 : 1;
+    constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
-    constexpr int kSides = kDirs;              // one B/C tile per token order
+    constexpr int kSides = kDirs;              // one B/C tile per direction
     __shared__ __attribute__((aligned(16))) float tile[2][kSides][2][kRowLanes][kTilePad];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
     const int row_in_wg = tid >> 4;           // 0..15
     const int n = lane & (kRowLanes - 1);     // state index, also token slot
-    const int dir = row_in_wg % kDirs;
-    const int ch = row_in_wg / kDirs;
+    // the wave index is uniform: reading it through readfirstlane lets the
+    // per-wave tensor choices below live in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool colpair = MODE == kModeCross4 && wave >= 2;
+    int dir, ch;
+    if (MODE == kModeCross4) {
+        const int r4 = row_in_wg & 3;
+        ch = ((wave & 1) << 1) | (r4 >> 1);
+        dir = (colpair ? 2 : 0) | (r4 & 1);
+    } else {
+        dir = row_in_wg % kDirs;
+        ch = row_in_wg / kDirs;
+    }
     const int64_t b = blockIdx.y;
     const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChPerWg + ch;
     const bool active = d0 < a.dim;
     const int64_t d = active ? d0 : 0;
     const int L = static_cast<int>(a.L);
     const int nblk = a.nblk;
-    const bool rev = MODE == kModeVim ? dir == 1 : a.reverse != 0;
+    const bool rev = MODE == kMode1D ? a.reverse != 0 : (dir & 1) != 0;
+    const int pside = dir & 1;                // position within the pair
 
     // per-row parameters
-    const int64_t prow = (MODE == kModeVim ? dir * a.dim : 0) + d;
+    const int64_t prow = (MODE == kMode1D ? 0 : dir * a.dim) + d;
     const float A2 = (active && n < a.dstate) ? a.A[prow * a.dstate + n] * kLog2e : 0.f;
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
@@ -241,11 +260,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // address arithmetic out of the loop.
     constexpr uint32_t kEs = sizeof(T);
     const uint32_t rowoff = static_cast<uint32_t>((b * a.dim + d) * a.L);
-    const char* __restrict__ ub = static_cast<const char*>(a.u);
-    const char* __restrict__ db = static_cast<const char*>(a.delta);
+    const char* __restrict__ ub = static_cast<const char*>(colpair ? a.uT : a.u);
+    const char* __restrict__ db = static_cast<const char*>(colpair ? a.deltaT : a.delta);
     const char* __restrict__ zb = static_cast<const char*>(a.z);
     char* __restrict__ yb = static_cast<char*>(a.y);
-    char* __restrict__ pb = reinterpret_cast<char*>(a.partial);
+    char* __restrict__ pb = reinterpret_cast<char*>(colpair ? a.partial2 : a.partial);
     auto act_at = [&](const char* base, int p) {
         return ld_raw(reinterpret_cast<const T*>(base + (rowoff + static_cast<uint32_t>(p)) * kEs), 0);
     };
@@ -259,10 +278,14 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // ---- B/C staging: thread (sn = tid/16, slot = tid%16) copies entry
     // (state sn, token slot) of every (side, B|C) tile. Rows of states >=
     // dstate stay zero (written once), so those state lanes never change.
+    // Vim's two sides read the shared B/C at tokens t and L-1-t; each
+    // cross-scan direction reads its own B/C, stored in its scan order.
     constexpr int kStage = kSides * 2;
     const int sn = tid >> 4, slot = tid & 15;
     const bool sn_ok = sn < a.dstate;
-    const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
+    const int64_t bc_dirs = MODE == kModeCross4 ? 4 : 1;
+    const uint32_t bc_row = static_cast<uint32_t>((b * bc_dirs * a.dstate + (sn_ok ? sn : 0)) * a.L);
+    const uint32_t bc_dir_stride = static_cast<uint32_t>(a.dstate * a.L);
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
     const char* __restrict__ Cb = static_cast<const char*>(a.C);
     auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
@@ -270,8 +293,14 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int tc = t < L ? t : L - 1;     // padding slots: any valid entry
 #pragma unroll
         for (int r = 0; r < kStage; ++r) {
-            const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
-            const uint32_t off = (bc_row + static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
+            uint32_t off;
+            if (MODE == kModeCross4) {
+                off = (bc_row + static_cast<uint32_t>(r >> 1) * bc_dir_stride +
+                       static_cast<uint32_t>(tc)) * kEs;
+            } else {
+                const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
+                off = (bc_row + static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
+            }
             sr[r] = ld_raw(reinterpret_cast<const T*>(((r & 1) ? Cb : Bb) + off), 0);
         }
     };
@@ -291,23 +320,29 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
     }
 
-    // ---- this lane's token of a block (slot n); unconditional loads on a
-    // clamped index so that they can all be in flight together.
-    const int Fstep = MODE == kModeVim ? (L - 1) / (2 * kBlockTok) : -1;
-    struct Tok { uint32_t u, dl, z; };
+    // ---- this lane's token of a block (slot n), clamped into the sequence;
+    // for the column-major pair it indexes the transposed copies
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
         const int tc = t < L ? t : L - 1;
         return rev ? L - 1 - tc : tc;
     };
+
+    // ---- this lane's token of a block; unconditional loads on a valid
+    // index so that they can all be in flight together.
+    const int Fstep = MODE != kMode1D ? (L - 1) / (2 * kBlockTok) : -1;
+    struct Tok { uint32_t u, dl, z; int p; };
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
+        k.p = p;
         k.u = act_at(ub, p);
         k.dl = act_at(db, p);
         // z is needed only by the visit that finishes the token; other
         // blocks load entry 0 of the row (one cached line) instead of
-        // branching, which would stall on the in-flight registers
-        if (GATE) k.z = act_at(zb, (MODE != kModeVim || blk >= Fstep) ? p : 0);
+        // branching, which would stall on the in-flight registers. The
+        // cross-scan gates after the loop.
+        if (GATE && MODE != kModeCross4)
+            k.z = act_at(zb, (MODE != kModeVim || blk >= Fstep) ? p : 0);
     };
 
     uint32_t sr[kStage];
@@ -325,14 +360,14 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // the two so that no register of an in-flight load is ever copied.
     auto step = [&](const int blk, Tok& cur, Tok& nxt) {
         const int buf = blk & 1;
-        const int p = tok_pos(blk);
+        const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
         // the other direction's partial sum, for blocks after step F (it was
         // stored at step F or earlier, before F's fence); earlier blocks load
         // entry 0 of the row instead (unused) rather than branch. Issued
         // before the prefetch so that waiting for it does not wait for those.
         float part = 0.f;
-        if (MODE == kModeVim)
+        if (MODE != kMode1D)
             part = __hip_atomic_load(part_at(blk > Fstep ? p : 0), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
         // prefetch the next block; on the last step this reloads the last
@@ -348,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
         const float du = dlt * cu;
 
-        const int side = MODE == kModeVim ? dir : 0;
+        const int side = MODE == kMode1D ? 0 : dir;
         const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][side][0][n][0]);
         const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][side][1][n][0]);
         float Bv[16], Cv[16];
@@ -366,27 +401,33 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             c[i] = Cv[i] * h;
         });
         const float yk = fmaf(Dk, cu, row_transpose_sum(c, lane));
-        const float gate = GATE ? silu_f(from_raw<T>(cur.z)) : 1.f;
+        const float gate = (GATE && MODE != kModeCross4) ? silu_f(from_raw<T>(cur.z)) : 1.f;
+        // a token's second visit: Vim gates and stores y, the cross-scan
+        // stores the pair's fp32 sum
+        auto finish = [&](float sum) {
+            if (MODE == kModeCross4) *part_at(p) = sum;
+            else st(y_at(p), 0, sum * gate);
+        };
 
         if (MODE == kMode1D) {
             if (ok) st(y_at(p), 0, yk * gate);
         } else if (blk < Fstep) {
             if (ok) *part_at(p) = yk;
         } else if (blk > Fstep) {
-            if (ok) st(y_at(p), 0, (yk + part) * gate);
+            if (ok) finish(yk + part);
         } else {
             // step F: tokens finished by the other direction in an earlier
             // step, or (forward row) shared with the backward row in this one
             const int t_self = blk * kBlockTok + n;
             const int blk_other = (L - 1 - t_self) / kBlockTok;
-            const bool first = blk < blk_other || (blk == blk_other && dir == 0);
+            const bool first = blk < blk_other || (blk == blk_other && pside == 0);
             if (ok && first)
                 __hip_atomic_store(part_at(p), yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
             if (ok && !first) {
                 const float other = __hip_atomic_load(part_at(p), __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-                st(y_at(p), 0, (yk + other) * gate);
+                finish(yk + other);
             }
         }
 
@@ -402,6 +443,89 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         step(blk + 1, tB, tA);
     }
     if (blk < nblk) step(blk, tA, tB);
+
+    if constexpr (MODE == kModeCross4) {
+        // every pair sum of the workgroup's channels is stored: y = (row-major
+        // pair + column-major pair) * gate. The column-major sums are in
+        // column-major order: 32 x 32 tiles of the grid pass through LDS,
+        // read along columns and written along rows.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        float (*tr)[kTrPad] = reinterpret_cast<float (*)[kTrPad]>(&tile[0][0][0][0][0]);
+        const char* __restrict__ p0 = reinterpret_cast<const char*>(a.partial);
+        const char* __restrict__ p1 = reinterpret_cast<const char*>(a.partial2);
+        const int H = a.H, Wd = a.W;
+        const int tx = tid & (kTr - 1), ty = tid / kTr;
+        const int tiles_w = (Wd + kTr - 1) / kTr, ntiles = tiles_w * ((H + kTr - 1) / kTr);
+        const int64_t dfirst = static_cast<int64_t>(blockIdx.x) * kChPerWg;
+        for (int c = 0; c < kChPerWg; ++c) {
+            if (dfirst + c >= a.dim) break;
+            const uint32_t off = static_cast<uint32_t>((b * a.dim + dfirst + c) * a.L);
+            for (int tile_id = 0; tile_id < ntiles; ++tile_id) {
+                const int i0 = (tile_id / tiles_w) * kTr, j0 = (tile_id % tiles_w) * kTr;
+#pragma unroll
+                for (int r = ty; r < kTr; r += kThreads / kTr) {
+                    const int i = i0 + tx, j = j0 + r;        // column j, row i
+                    if (i < H && j < Wd) {
+                        const uint32_t o = off + static_cast<uint32_t>(j * H + i);
+                        tr[r][tx] = __hip_atomic_load(reinterpret_cast<const float*>(p1 + o * 4u),
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+                for (int r = ty; r < kTr; r += kThreads / kTr) {
+                    const int i = i0 + r, j = j0 + tx;        // row i, column j
+                    if (i < H && j < Wd) {
+                        const uint32_t o = off + static_cast<uint32_t>(i * Wd + j);
+                        float v = __hip_atomic_load(reinterpret_cast<const float*>(p0 + o * 4u),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
+                                  tr[tx][r];
+                        if (GATE)
+                            v *= silu_f(from_raw<T>(ld_raw(reinterpret_cast<const T*>(zb + o * kEs), 0)));
+                        st(reinterpret_cast<T*>(yb + o * kEs), 0, v);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            }
+        }
+    }
+}
+
+// Transpose u and delta of every (batch, channel) from the row-major H x W
+// grid to column-major order (entry j*H + i = grid element (i, j)), in 32 x
+// 32 tiles through LDS so that reads and writes are both contiguous.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void grid_transpose_kernel(
+    const T* __restrict__ u, const T* __restrict__ dl, T* __restrict__ uT, T* __restrict__ dT,
+    int H, int W, int64_t nrows) {
+    __shared__ T tr[kTr][kTr + 1];
+    const T* __restrict__ src = blockIdx.z ? dl : u;
+    T* __restrict__ dst = blockIdx.z ? dT : uT;
+    const int tiles_w = (W + kTr - 1) / kTr;
+    const int i0 = (blockIdx.x / tiles_w) * kTr, j0 = (blockIdx.x % tiles_w) * kTr;
+    const int tx = threadIdx.x & (kTr - 1), ty = threadIdx.x / kTr;
+    const int64_t L = static_cast<int64_t>(H) * W;
+    for (int64_t row = blockIdx.y; row < nrows; row += gridDim.y) {
+        const int64_t base = row * L;
+#pragma unroll
+        for (int r = ty; r < kTr; r += kThreads / kTr) {
+            const int i = i0 + r, j = j0 + tx;
+            if (i < H && j < W) tr[r][tx] = src[base + static_cast<int64_t>(i) * W + j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = ty; r < kTr; r += kThreads / kTr) {
+            const int j = j0 + r, i = i0 + tx;
+            if (i < H && j < W) dst[base + static_cast<int64_t>(j) * H + i] = tr[tx][r];
+        }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------- host side
@@ -492,17 +616,39 @@ int launch_t(const Call& c) {
     ScanArgs a;
     a.u = c.u; a.delta = c.delta; a.z = c.z; a.B = c.B; a.C = c.C;
     a.A = c.A; a.Dskip = c.Dskip; a.dt_bias = c.dt_bias; a.y = c.y;
-    a.partial = c.dtype == VS_F32 ? static_cast<float*>(c.y) : static_cast<float*>(c.ws);
+    // merge buffers: fp32 y doubles as the first one; the cross-scan's second
+    // pair always uses the workspace (after the first buffer if y is bf16)
+    float* ws = static_cast<float*>(c.ws);
+    const int64_t elems = c.batch * c.dim * c.L;
+    a.partial = c.dtype == VS_F32 ? static_cast<float*>(c.y) : ws;
+    a.partial2 = nullptr;
+    a.uT = a.deltaT = nullptr;
+    if (MODE == kModeCross4) {
+        // workspace: [bf16 only: pair-0 sums][pair-1 sums][u^T][delta^T]
+        a.partial2 = c.dtype == VS_F32 ? ws : ws + elems;
+        T* act = reinterpret_cast<T*>(a.partial2 + elems);
+        a.uT = act;
+        a.deltaT = act + elems;
+    }
     a.dim = c.dim; a.L = c.L; a.H = c.H; a.W = c.W;
     a.dstate = static_cast<int>(c.dstate);
     a.softplus = c.softplus ? 1 : 0;
     a.reverse = c.reverse ? 1 : 0;
     a.nblk = static_cast<int>((c.L + kBlockTok - 1) / kBlockTok);
-    constexpr int kChPerWg = MODE == kModeVim ? 8 : 16;
+    constexpr int kChPerWg = MODE == kModeVim ? 8 : (MODE == kModeCross4 ? 4 : 16);
     dim3 grid(static_cast<unsigned>((c.dim + kChPerWg - 1) / kChPerWg),
               static_cast<unsigned>(c.batch));
     hipStream_t st = static_cast<hipStream_t>(c.stream);
     const dim3 blk(kThreads);
+    if (MODE == kModeCross4) {
+        const int64_t rows = c.batch * c.dim;
+        const unsigned tiles = static_cast<unsigned>(((c.H + kTr - 1) / kTr) * ((c.W + kTr - 1) / kTr));
+        const unsigned gy = static_cast<unsigned>(rows < 65535 ? rows : 65535);
+        hipLaunchKernelGGL((grid_transpose_kernel<T>), dim3(tiles, gy, 2), blk, 0, st,
+                           static_cast<const T*>(c.u), static_cast<const T*>(c.delta),
+                           const_cast<T*>(static_cast<const T*>(a.uT)),
+                           const_cast<T*>(static_cast<const T*>(a.deltaT)), c.H, c.W, rows);
+    }
     if (c.z && c.softplus)
         hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, true>), grid, blk, 0, st, a);
     else if (c.z)
@@ -524,7 +670,7 @@ int run(const Call& c) {
     switch (c.mode) {
     case kMode1D: return bf ? launch_t<uint16_t, kMode1D>(c) : launch_t<float, kMode1D>(c);
     case kModeVim: return bf ? launch_t<uint16_t, kModeVim>(c) : launch_t<float, kModeVim>(c);
-    default: return fail(VS_ERR_UNSUPPORTED, "cross-scan is not built yet");
+    default: return bf ? launch_t<uint16_t, kModeCross4>(c) : launch_t<float, kModeCross4>(c);
     }
 }
 
@@ -535,10 +681,17 @@ extern "C" {
 
 size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype) {
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
-    if (dtype != VS_BF16) return 0;            // fp32 y holds the partial sums
-    if (op == VS_OP_VIM_BIDIR || op == VS_OP_CROSS4)
-        return static_cast<size_t>(batch * dim * seqlen) * sizeof(float);
-    return 0;
+    if (dtype != VS_F32 && dtype != VS_BF16) return 0;
+    // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
+    // cross-scan two; an fp32 y serves as the first. The cross-scan also
+    // keeps column-major copies of u and delta (input dtype).
+    const int64_t elems = batch * dim * seqlen;
+    const int64_t bufs = (op == VS_OP_VIM_BIDIR ? 1 : (op == VS_OP_CROSS4 ? 2 : 0)) -
+                         (dtype == VS_F32 ? 1 : 0);
+    const int64_t copies = op == VS_OP_CROSS4 ? 2 : 0;
+    const int64_t es = dtype == VS_BF16 ? 2 : 4;
+    if (bufs <= 0 && copies == 0) return 0;
+    return static_cast<size_t>(elems * (4 * (bufs > 0 ? bufs : 0) + es * copies));
 }
 
 int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
