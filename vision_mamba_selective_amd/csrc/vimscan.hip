@@ -173,6 +173,22 @@ __device__ __forceinline__ float silu_f(float z) {
     return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// Workgroups are dispatched to the 8 XCDs (each with its own L2) round-robin
+// by linear id. Renumber them so that every XCD receives one contiguous range
+// of (batch, channel-group) ids: the workgroups that share a batch's B and C
+// then mostly share one L2. A bijection on [0, G): XCD x gets the linear ids
+// x, x+8, ..., which map to the range starting at x*(G/8) + min(x, G%8).
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ void xcd_block(uint32_t& cg, uint32_t& bb) {
+    const uint32_t G = gridDim.x * gridDim.y;
+    const uint32_t lin = blockIdx.x + blockIdx.y * gridDim.x;
+    const uint32_t x = lin % kXcds, k = lin / kXcds;
+    const uint32_t q = G / kXcds, r = G % kXcds;
+    const uint32_t v = x * q + (x < r ? x : r) + k;
+    cg = v % gridDim.x;
+    bb = v / gridDim.x;
+}
+
 template <int I>
 struct Unroll {
     template <typename F>
@@ -241,8 +257,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         dir = row_in_wg % kDirs;
         ch = row_in_wg / kDirs;
     }
-    const int64_t b = blockIdx.y;
-    const int64_t d0 = static_cast<int64_t>(blockIdx.x) * kChPerWg + ch;
+    uint32_t cg, bb;
+    xcd_block(cg, bb);
+    const int64_t b = bb;
+    const int64_t d0 = static_cast<int64_t>(cg) * kChPerWg + ch;
     const bool active = d0 < a.dim;
     const int64_t d = active ? d0 : 0;
     const int L = static_cast<int>(a.L);
@@ -458,7 +476,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int H = a.H, Wd = a.W;
         const int tx = tid & (kTr - 1), ty = tid / kTr;
         const int tiles_w = (Wd + kTr - 1) / kTr, ntiles = tiles_w * ((H + kTr - 1) / kTr);
-        const int64_t dfirst = static_cast<int64_t>(blockIdx.x) * kChPerWg;
+        const int64_t dfirst = static_cast<int64_t>(cg) * kChPerWg;
         for (int c = 0; c < kChPerWg; ++c) {
             if (dfirst + c >= a.dim) break;
             const uint32_t off = static_cast<uint32_t>((b * a.dim + dfirst + c) * a.L);
