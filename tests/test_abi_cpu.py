@@ -119,6 +119,18 @@ def test_cross4_validation(nat):
     assert f(1, 4, 16, 1 << 21, 7, nat.VS_F32, *args) == -2
 
 
+def test_element_limit(nat):
+    """Activation tensors of 2^30 elements or more are refused (the kernels
+    address them with 32-bit byte offsets); one element fewer is accepted
+    by validation (checked here up to the workspace test only)."""
+    far = lambda i: BASE + i * (8 << 30)    # 8 GiB apart: no overlap at this size
+    big = dict(u=far(0), delta=far(1), z=far(2), B=far(3), C=far(4), A=far(5), D=far(6),
+               bias=far(7), y=far(8), ws=far(9), ws_bytes=1 << 33)
+    assert vim_call(nat, batch=1, dim=16384, L=65536, **big) == -6
+    big["ws"] = None
+    assert vim_call(nat, batch=1, dim=16384, L=65535, **big) == -8
+
+
 def test_1d_validation(nat):
     f = nat.lib.s6_scan_1d
     assert f(1, 4, 16, 10, nat.VS_F32, 0, None, fake(1), None, fake(3), fake(4), fake(5),
