@@ -52,6 +52,11 @@ def _bind(lib):
     Lg = ctypes.c_long
     lib.oracle_scan_f64.argtypes = [I, I, I, Lg, Lg, Lg, I, P, P, P, P, P, P, I, P, P, P, I, P, I]
     lib.oracle_scan_f64.restype = I
+    lib.oracle_scan_ex_f64.argtypes = [I, I, I, Lg, Lg, Lg, I, P, P, I, P, P, P, P, I, P, P, P, I,
+                                       P, I]
+    lib.oracle_scan_ex_f64.restype = I
+    lib.oracle_vim_conv_f64.argtypes = [I, I, I, Lg, P, P, P, P, P, P, P, P, P, P, I, P, I]
+    lib.oracle_vim_conv_f64.restype = I
     return lib
 
 
@@ -74,20 +79,22 @@ def _ptr(a):
 
 def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
          bc_per_direction: bool, H: int = 0, W: int = 0, delta_softplus: bool = True,
-         nthreads: Optional[int] = None, lib=None) -> np.ndarray:
+         nthreads: Optional[int] = None, lib=None, u_per_direction: bool = False) -> np.ndarray:
     """Generic scan: len(orders) directions, merged by sum, optional gate.
 
-    u, delta, z: [batch, dim, L]; B, C: [batch, dstate, L] (shared, token
-    order) or [batch, ndir, dstate, L] (per direction, scan order);
+    u, delta, z: [batch, dim, L] (u: [ndir, batch, dim, L] when
+    u_per_direction); B, C: [batch, dstate, L] (shared, token order) or
+    [batch, ndir, dstate, L] (per direction, scan order);
     A: [ndir, dim, dstate]; Dskip, dt_bias: [ndir, dim] or None.
     """
     lib = lib or load()
     u, delta, z, B, C, A = map(_f64, (u, delta, z, B, C, A))
     Dskip, dt_bias = _f64(Dskip), _f64(dt_bias)
-    batch, dim, L = u.shape
+    batch, dim, L = delta.shape
     ndir = len(orders)
+    assert u.shape == ((ndir,) if u_per_direction else ()) + (batch, dim, L)
     dstate = A.shape[-1]
-    assert delta.shape == u.shape and (z is None or z.shape == u.shape)
+    assert z is None or z.shape == delta.shape
     assert A.shape == (ndir, dim, dstate)
     if bc_per_direction:
         assert B.shape == (batch, ndir, dstate, L) and C.shape == B.shape
@@ -97,12 +104,13 @@ def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
         assert p is None or p.shape == (ndir, dim)
     order = np.ascontiguousarray(orders, dtype=np.intc)
     y = np.empty((batch, dim, L), np.float64)
-    rc = lib.oracle_scan_f64(batch, dim, dstate, L, H, W, ndir, _ptr(order), _ptr(u),
-                             _ptr(delta), _ptr(z), _ptr(B), _ptr(C), int(bc_per_direction),
-                             _ptr(A), _ptr(Dskip), _ptr(dt_bias), int(bool(delta_softplus)),
-                             _ptr(y), nthreads or default_threads())
+    rc = lib.oracle_scan_ex_f64(batch, dim, dstate, L, H, W, ndir, _ptr(order), _ptr(u),
+                                int(bool(u_per_direction)), _ptr(delta), _ptr(z), _ptr(B),
+                                _ptr(C), int(bc_per_direction), _ptr(A), _ptr(Dskip),
+                                _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y),
+                                nthreads or default_threads())
     if rc != 0:
-        raise ValueError("oracle_scan_f64 failed with status %d" % rc)
+        raise ValueError("oracle_scan_ex_f64 failed with status %d" % rc)
     return y
 
 
@@ -110,6 +118,29 @@ def vim_bidir(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthread
     """Vim: forward + backward over shared u, delta, z, B, C."""
     return scan(u, delta, z, B, C, A, Dskip, dt_bias, orders=(ORD_FORWARD, ORD_REVERSE),
                 bc_per_direction=False, delta_softplus=delta_softplus, nthreads=nthreads)
+
+
+def vim_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True,
+             nthreads=None, lib=None):
+    """Vim with its conv front end: u_f = silu(conv_f(x)), u_b the flipped
+    branch's silu(conv_b(flip x)). x: [batch, dim, L]; conv_w: [2, dim, 3];
+    conv_b: [2, dim] or None; the rest as for vim_bidir."""
+    lib = lib or load()
+    x, conv_w, conv_b, delta, z, B, C, A = map(_f64, (x, conv_w, conv_b, delta, z, B, C, A))
+    Dskip, dt_bias = _f64(Dskip), _f64(dt_bias)
+    batch, dim, L = x.shape
+    dstate = A.shape[-1]
+    assert conv_w.shape == (2, dim, 3) and (conv_b is None or conv_b.shape == (2, dim))
+    assert delta.shape == x.shape and (z is None or z.shape == x.shape)
+    assert A.shape == (2, dim, dstate) and B.shape == (batch, dstate, L) and C.shape == B.shape
+    y = np.empty((batch, dim, L), np.float64)
+    rc = lib.oracle_vim_conv_f64(batch, dim, dstate, L, _ptr(x), _ptr(conv_w), _ptr(conv_b),
+                                 _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                 _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y),
+                                 nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_vim_conv_f64 failed with status %d" % rc)
+    return y
 
 
 def cross4(u, delta, z, B, C, A, Dskip, dt_bias, H, W, delta_softplus=True, nthreads=None):

@@ -76,6 +76,8 @@ typedef struct {
     const double *u, *delta, *z, *B, *C, *A, *Dskip, *dt_bias;
     int bc_per_direction;   /* 0: B, C are [batch][dstate][L] in token order;
                                1: [batch][ndir][dstate][L] in scan order */
+    int u_per_direction;    /* 0: u is [batch][dim][L], shared by the directions;
+                               1: [ndir][batch][dim][L], one per direction */
     int delta_softplus;
     double* y;
     /* work split */
@@ -88,13 +90,14 @@ static void run_unit(const job_t* J, long unit, double* h, double* acc)
 {
     const long b = unit / J->dim, d = unit % J->dim;
     const long L = J->L, N = J->dstate;
-    const double* u = J->u + (b * J->dim + d) * L;
     const double* dl = J->delta + (b * J->dim + d) * L;
     double* y = J->y + (b * J->dim + d) * L;
 
     for (long p = 0; p < L; ++p) acc[p] = 0.0;
 
     for (int k = 0; k < J->ndir; ++k) {
+        const double* u = J->u + (J->u_per_direction ? (long)k * J->batch * J->dim * L : 0)
+                          + (b * J->dim + d) * L;
         const double* A = J->A + ((long)k * J->dim + d) * N;
         const double Dk = J->Dskip ? J->Dskip[(long)k * J->dim + d] : 0.0;
         const double bias = J->dt_bias ? J->dt_bias[(long)k * J->dim + d] : 0.0;
@@ -146,13 +149,14 @@ static void* worker(void* arg)
     return NULL;
 }
 
-/* Generic entry: ndir directions with the given visiting orders.
+/* Generic entry: ndir directions with the given visiting orders; u shared
+ * (u_per_direction = 0) or one per direction (1).
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
-int oracle_scan_f64(int batch, int dim, int dstate, long L, long H, long W,
-                    int ndir, const int* order, const double* u, const double* delta,
-                    const double* z, const double* B, const double* C, int bc_per_direction,
-                    const double* A, const double* Dskip, const double* dt_bias,
-                    int delta_softplus, double* y, int nthreads)
+int oracle_scan_ex_f64(int batch, int dim, int dstate, long L, long H, long W,
+                       int ndir, const int* order, const double* u, int u_per_direction,
+                       const double* delta, const double* z, const double* B, const double* C,
+                       int bc_per_direction, const double* A, const double* Dskip,
+                       const double* dt_bias, int delta_softplus, double* y, int nthreads)
 {
     if (batch < 0 || dim < 0 || dstate < 1 || L < 0 || ndir < 1 || !order) return -1;
     if (batch == 0 || dim == 0 || L == 0) return 0;
@@ -175,6 +179,7 @@ int oracle_scan_f64(int batch, int dim, int dstate, long L, long H, long W,
         J->u = u; J->delta = delta; J->z = z; J->B = B; J->C = C;
         J->A = A; J->Dskip = Dskip; J->dt_bias = dt_bias;
         J->bc_per_direction = bc_per_direction; J->delta_softplus = delta_softplus;
+        J->u_per_direction = u_per_direction ? 1 : 0;
         J->y = y;
         J->unit_begin = units * i / nthreads;
         J->unit_end = units * (i + 1) / nthreads;
@@ -195,6 +200,72 @@ int oracle_scan_f64(int batch, int dim, int dstate, long L, long H, long W,
         if (worker(&jobs[i]) != NULL) rc = -2;
     free(jobs);
     free(th);
+    return rc;
+}
+
+/* The shared-u scan (the Vim and VMamba entries below use it). */
+int oracle_scan_f64(int batch, int dim, int dstate, long L, long H, long W,
+                    int ndir, const int* order, const double* u, const double* delta,
+                    const double* z, const double* B, const double* C, int bc_per_direction,
+                    const double* A, const double* Dskip, const double* dt_bias,
+                    int delta_softplus, double* y, int nthreads)
+{
+    return oracle_scan_ex_f64(batch, dim, dstate, L, H, W, ndir, order, u, 0, delta, z, B, C,
+                              bc_per_direction, A, Dskip, dt_bias, delta_softplus, y, nthreads);
+}
+
+/* Depthwise Conv1d with kernel 3, padding 1 and a bias, as the guide's
+ * BidirectionalVisionMambaBlock applies it (conv_f, conv_b; PyTorch's Conv1d
+ * is a cross-correlation): out[t] = bias + w[0] in[t-1] + w[1] in[t] +
+ * w[2] in[t+1], with in[-1] = in[L] = 0. */
+static void conv3(const double* in, long L, const double* w, double bias, double* out)
+{
+    for (long t = 0; t < L; ++t) {
+        const double left = t > 0 ? in[t - 1] : 0.0;
+        const double right = t + 1 < L ? in[t + 1] : 0.0;
+        out[t] = bias + w[0] * left + w[1] * in[t] + w[2] * right;
+    }
+}
+
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
+/* Vim with its front end: u_f = silu(conv_f(x)) feeds the forward scan and
+ * u_b = silu(conv_b(flip(x))), in the flipped order, feeds the backward scan
+ * (the guide's "1. Forward Branch" and "2. Backward Branch (Reverse
+ * sequence)"); the D skip of each direction uses its own u. conv_w is
+ * [2][dim][3], conv_b [2][dim] (NULL: no bias). u_b is stored back in token
+ * order (u_b[p] is the value the backward scan reads at token p). */
+int oracle_vim_conv_f64(int batch, int dim, int dstate, long L, const double* x,
+                        const double* conv_w, const double* conv_b, const double* delta,
+                        const double* z, const double* B, const double* C, const double* A,
+                        const double* Dskip, const double* dt_bias, int delta_softplus,
+                        double* y, int nthreads)
+{
+    if (batch < 0 || dim < 0 || L < 0 || !x || !conv_w) return -1;
+    if (batch == 0 || dim == 0 || L == 0) return 0;
+    const long rows = (long)batch * dim;
+    double* u = (double*)malloc(sizeof(double) * (size_t)(2 * rows * L));
+    double* rev = (double*)malloc(sizeof(double) * (size_t)L);
+    double* c = (double*)malloc(sizeof(double) * (size_t)L);
+    if (!u || !rev || !c) { free(u); free(rev); free(c); return -2; }
+    for (long r = 0; r < rows; ++r) {
+        const long d = r % dim;
+        const double* xr = x + r * L;
+        /* forward branch */
+        conv3(xr, L, conv_w + d * 3, conv_b ? conv_b[d] : 0.0, c);
+        for (long p = 0; p < L; ++p) u[r * L + p] = silu(c[p]);
+        /* backward branch: flip, convolve, SiLU; step t of the flipped
+         * sequence is token L-1-t */
+        for (long t = 0; t < L; ++t) rev[t] = xr[L - 1 - t];
+        conv3(rev, L, conv_w + ((long)dim + d) * 3, conv_b ? conv_b[dim + d] : 0.0, c);
+        for (long t = 0; t < L; ++t) u[(rows + r) * L + (L - 1 - t)] = silu(c[t]);
+    }
+    free(rev);
+    free(c);
+    const int order[2] = {ORD_FORWARD, ORD_REVERSE};
+    const int rc = oracle_scan_ex_f64(batch, dim, dstate, L, 0, 0, 2, order, u, 1, delta, z, B,
+                                      C, 0, A, Dskip, dt_bias, delta_softplus, y, nthreads);
+    free(u);
     return rc;
 }
 
