@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-channels", type=int, default=0,
                    help="channels per batch row in the CPU sample (0: whole workload)")
+    p.add_argument("--conv", action="store_true",
+                   help="time vim_scan_bidir_conv: the same scan with the Vim block's conv1d + "
+                        "SiLU front end fused into its token loads (u is then the conv input x)")
     p.add_argument("--copy-probe", action="store_true",
                    help="instead of the scan, run torch copies of known size (counter scale)")
     return p.parse_args()
@@ -86,6 +89,9 @@ def main():
 
     idx = wlm.HEADLINE if args.workload is None else args.workload
     wl = wlm.WORKLOADS[idx]
+    if args.conv and wl.kind != "vim":
+        print("--conv applies to the Vim workloads only", file=sys.stderr)
+        sys.exit(2)
     tdt = torch.bfloat16 if wl.dtype == wlm.BF16 else torch.float32
     print("bench: workload %s" % wl.name, file=sys.stderr, flush=True)
 
@@ -100,6 +106,12 @@ def main():
     base = dict(u=up(inp.u, tdt), delta=up(inp.delta, tdt), z=up(inp.z, tdt), B=up(inp.B, tdt),
                 C=up(inp.C, tdt), A=up(inp.A, torch.float32), D=up(inp.D, torch.float32),
                 bias=up(inp.dt_bias, torch.float32))
+    if args.conv:
+        crng = np.random.default_rng(wl.seed + 500)
+        base["cw"] = up((0.6 * crng.standard_normal((2, wl.dim, 3))).astype(np.float32),
+                        torch.float32)
+        base["cb"] = up((0.2 * crng.standard_normal((2, wl.dim))).astype(np.float32),
+                        torch.float32)
     for s in range(nsets):
         t = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
         t["y"] = torch.empty_like(t["u"])
@@ -110,7 +122,10 @@ def main():
         sets.append(t)
 
     def step(t):
-        if wl.kind == "vim":
+        if args.conv:
+            vms.vim_scan_bidir_conv(t["u"], t["cw"], t["cb"], t["delta"], t["z"], t["B"], t["C"],
+                                    t["A"], t["D"], t["bias"], out=t["y"], workspace=t["ws"])
+        elif wl.kind == "vim":
             vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
                                t["bias"], out=t["y"], workspace=t["ws"])
         else:
@@ -150,7 +165,7 @@ def main():
         try:
             with open(PROFILE_TRAFFIC) as f:
                 tr = json.load(f)
-            rec = tr.get(wl.name)
+            rec = tr.get(wl.name + ("+conv" if args.conv else ""))
             if rec and rec.get("kernel_sha") == kernel_hash():
                 traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -171,7 +186,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "kind": wl.kind, "batch": wl.batch, "d_inner": wl.dim,
                    "d_state": wl.dstate, "seq_len": wl.seqlen, "directions": wl.ndir,
-                   "state_dtype": "f32", "input_sets_rotated": nsets},
+                   "state_dtype": "f32", "input_sets_rotated": nsets,
+                   "front_end": "conv1d k3 + silu, fused" if args.conv else "none"},
         "hbm_GBps": round(hbm_gbs, 1),
         "kernel_ms": round(kern_avg_s * 1e3, 5),
         "roofline": {
@@ -192,11 +208,14 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels)
+        conv = None
+        if args.conv:
+            conv = (base["cw"].cpu().numpy(), base["cb"].cpu().numpy())
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, nch):
+def cpu_baseline(wl, inp, nch, conv=None):
     """The fp64 oracle, as it stands, on the host cores of this machine."""
     import oracle
     from vision_mamba_selective_amd import workloads as wlm
@@ -211,7 +230,13 @@ def cpu_baseline(wl, inp, nch):
           flush=True)
     oracle.load()
     t0 = time.perf_counter()
-    oracle.run_inputs(sample, nthreads=threads)
+    if conv is None:
+        oracle.run_inputs(sample, nthreads=threads)
+    else:
+        w, b = conv
+        ch = list(range(sample.wl.dim))
+        oracle.vim_conv(sample.u, w[:, ch], b[:, ch], sample.delta, sample.z, sample.B, sample.C,
+                        sample.A, sample.D, sample.dt_bias, nthreads=threads)
     dt = time.perf_counter() - t0
     cpu = "unknown"
     try:

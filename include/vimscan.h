@@ -111,6 +111,30 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    void* stream);
 
 /*
+ * vim_scan_bidir with the Vim block's front end fused into the token loads:
+ * each branch's scan input is u_k = silu(conv_k(x)), a depthwise Conv1d with
+ * kernel 3, padding 1 and bias, applied to x in the forward branch and to
+ * the flipped sequence in the backward branch (section "1. PyTorch
+ * Implementation of the Bidirectional Vision Mamba Block": conv_f, conv_b and
+ * the "Forward Branch" / "Backward Branch (Reverse sequence)" steps). Each
+ * direction's D skip uses its own u_k; u is never written to memory.
+ *   x              [batch][dim][L] (input dtype), takes the place of u
+ *   conv_w         [2][dim][3] fp32: taps of direction k (0 forward,
+ *                  1 backward) for channel d; in each branch's own order,
+ *                  out[q] = b + w[0] in[q-1] + w[1] in[q] + w[2] in[q+1],
+ *                  in[-1] = in[L] = 0 (PyTorch's Conv1d)
+ *   conv_b         [2][dim] fp32, or NULL for zeros
+ *   everything else as for vim_scan_bidir (same workspace).
+ * Returns VS_ERR_NULL when conv_w is NULL.
+ */
+int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* x, const float* conv_w, const float* conv_b,
+                        const void* delta, const void* z, const void* B, const void* C,
+                        const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * VMamba four-direction cross-scan of an H x W grid (L = H*W tokens, stored
  * row-major: token p = i*W + j). Direction 0 visits p = t, 1 visits
  * p = L-1-t, 2 visits the columns top to bottom, left to right

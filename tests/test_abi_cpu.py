@@ -25,7 +25,8 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for required in ("vim_scan_bidir", "vmamba_cross_scan4", "s6_scan_1d", "vs_strerror",
+    for required in ("vim_scan_bidir", "vim_scan_bidir_conv", "vmamba_cross_scan4",
+                     "s6_scan_1d", "vs_strerror",
                      "vs_last_error", "vs_abi_version", "vs_workspace_bytes"):
         assert required in names
 
@@ -129,6 +130,20 @@ def test_element_limit(nat):
     assert vim_call(nat, batch=1, dim=16384, L=65536, **big) == -6
     big["ws"] = None
     assert vim_call(nat, batch=1, dim=16384, L=65535, **big) == -8
+
+
+def test_conv_validation(nat):
+    f = nat.lib.vim_scan_bidir_conv
+    def call(**kw):
+        a = dict(x=fake(0), w=fake(10), b=None, y=fake(8), ws=fake(9))
+        a.update(kw)
+        return f(2, 8, 16, 33, nat.VS_BF16, a["x"], a["w"], a["b"], fake(1), fake(2), fake(3),
+                 fake(4), fake(5), fake(6), fake(7), 1, a["y"], a["ws"], 1 << 20, None)
+    assert call(w=None) == -1
+    assert call(w=fake(10) + 2) == -4
+    assert call(b=fake(11) + 1) == -4
+    assert call(y=fake(10) - 64) == -5          # y runs into conv_w
+    assert call(x=None) == -1
 
 
 def test_1d_validation(nat):

@@ -63,6 +63,8 @@ struct ScanArgs {
     float* partial2;    // cross-scan: the column-major pair's partial sums
     const void* uT;     // cross-scan: u and delta transposed to column-major
     const void* deltaT;
+    const float* conv_w;    // Vim front end: depthwise taps [2][dim][3] (u holds x)
+    const float* conv_b;    // and biases [2][dim] (NULL: 0)
     int64_t dim;
     int64_t L;
     int H;
@@ -233,8 +235,9 @@ struct Unroll<0> {
 // sums are read only after it. Vim finishes a token by gating and storing
 // y; the cross-scan stores the pair's sum, and after the loop the workgroup
 // adds its two pairs' sums, gates and stores y.
-template <typename T, int MODE, bool GATE, bool SOFTPLUS>
+template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
+    static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
@@ -273,6 +276,19 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const float A2 = (active && n < a.dstate) ? a.A[prow * a.dstate + n] * kLog2e : 0.f;
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
+    // Vim front end: each branch's u = silu(b + w0 x[q-1] + w1 x[q] + w2 x[q+1])
+    // over its own sequence order q, with zeros past the ends ("1. Forward
+    // Branch", "2. Backward Branch (Reverse sequence)"). In token order the
+    // backward branch's left neighbour is token p+1, so its taps are
+    // mirrored: cw_l multiplies x[p-1], cw_r multiplies x[p+1].
+    float cw_l = 0.f, cw_c = 0.f, cw_r = 0.f, cw_b = 0.f;
+    if (CONV && active) {
+        const float* w = a.conv_w + prow * 3;
+        cw_l = rev ? w[2] : w[0];
+        cw_c = w[1];
+        cw_r = rev ? w[0] : w[2];
+        cw_b = a.conv_b ? a.conv_b[prow] : 0.f;
+    }
     // Every tensor is addressed as its scalar base address plus a 32-bit
     // byte offset (tensors stay below 4 GiB), which keeps per-lane 64-bit
     // address arithmetic out of the loop.
@@ -349,11 +365,15 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // ---- this lane's token of a block; unconditional loads on a valid
     // index so that they can all be in flight together.
     const int Fstep = MODE != kMode1D ? (L - 1) / (2 * kBlockTok) : -1;
-    struct Tok { uint32_t u, dl, z; int p; };
+    struct Tok { uint32_t u, dl, z, ul, ur; int p; };
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
         k.p = p;
         k.u = act_at(ub, p);
+        if (CONV) {   // the neighbours (clamped; masked where they fall outside)
+            k.ul = act_at(ub, p > 0 ? p - 1 : 0);
+            k.ur = act_at(ub, p < L - 1 ? p + 1 : L - 1);
+        }
         k.dl = act_at(db, p);
         // z is needed only by the visit that finishes the token; other
         // blocks load entry 0 of the row (one cached line) instead of
@@ -396,7 +416,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 
         // delta and delta*u of this lane's token (zero in padding slots, which
         // then leave the state unchanged: exp(0) = 1 and no input)
-        const float cu = from_raw<T>(cur.u);
+        float cu = from_raw<T>(cur.u);
+        if (CONV) {
+            const float xl = p > 0 ? from_raw<T>(cur.ul) : 0.f;
+            const float xr = p < L - 1 ? from_raw<T>(cur.ur) : 0.f;
+            cu = silu_f(fmaf(cw_l, xl, fmaf(cw_c, cu, fmaf(cw_r, xr, cw_b))));
+        }
         const float x = from_raw<T>(cur.dl) + bias;
         const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
         const float du = dlt * cu;
@@ -575,6 +600,8 @@ struct Call {
     void* ws;
     size_t ws_bytes;
     void* stream;
+    const float* conv_w = nullptr;   // Vim front end (u then holds x)
+    const float* conv_b = nullptr;
 };
 
 int64_t ndirs(int mode) { return mode == kModeVim ? 2 : (mode == kModeCross4 ? 4 : 1); }
@@ -599,7 +626,7 @@ int validate(const Call& c) {
     const void* acts[] = {c.u, c.delta, c.z, c.B, c.C, c.y};
     for (const void* p : acts)
         if (p && !aligned(p, es)) return fail(VS_ERR_ALIGN, "activation pointer misaligned");
-    const void* fparams[] = {c.A, c.Dskip, c.dt_bias, c.ws};
+    const void* fparams[] = {c.A, c.Dskip, c.dt_bias, c.ws, c.conv_w, c.conv_b};
     for (const void* p : fparams)
         if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
     const int64_t nd = ndirs(c.mode);
@@ -608,9 +635,11 @@ int validate(const Call& c) {
                                           c.L) * es;
     const size_t a_bytes = static_cast<size_t>(nd * c.dim * c.dstate) * 4;
     const size_t p_bytes = static_cast<size_t>(nd * c.dim) * 4;
-    const void* ins[] = {c.u, c.delta, c.z, c.B, c.C, c.A, c.Dskip, c.dt_bias};
-    const size_t in_bytes[] = {act, act, act, bc, bc, a_bytes, p_bytes, p_bytes};
-    for (int i = 0; i < 8; ++i)
+    const void* ins[] = {c.u, c.delta, c.z, c.B, c.C, c.A, c.Dskip, c.dt_bias, c.conv_w, c.conv_b};
+    const size_t in_bytes[] = {act, act, act, bc, bc, a_bytes, p_bytes, p_bytes, 3 * p_bytes,
+                               p_bytes};
+    constexpr int kIns = 10;
+    for (int i = 0; i < kIns; ++i)
         if (overlaps(c.y, act, ins[i], in_bytes[i]))
             return fail(VS_ERR_ALIAS, "y overlaps an input");
     const size_t need = vs_workspace_bytes(
@@ -620,7 +649,7 @@ int validate(const Call& c) {
         if (!c.ws || c.ws_bytes < need)
             return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
         if (overlaps(c.y, act, c.ws, need)) return fail(VS_ERR_ALIAS, "y overlaps the workspace");
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < kIns; ++i)
             if (overlaps(c.ws, need, ins[i], in_bytes[i]))
                 return fail(VS_ERR_ALIAS, "workspace overlaps an input");
     }
@@ -634,6 +663,7 @@ int launch_t(const Call& c) {
     ScanArgs a;
     a.u = c.u; a.delta = c.delta; a.z = c.z; a.B = c.B; a.C = c.C;
     a.A = c.A; a.Dskip = c.Dskip; a.dt_bias = c.dt_bias; a.y = c.y;
+    a.conv_w = c.conv_w; a.conv_b = c.conv_b;
     // merge buffers: fp32 y doubles as the first one; the cross-scan's second
     // pair always uses the workspace (after the first buffer if y is bf16)
     float* ws = static_cast<float*>(c.ws);
@@ -667,7 +697,16 @@ int launch_t(const Call& c) {
                            const_cast<T*>(static_cast<const T*>(a.uT)),
                            const_cast<T*>(static_cast<const T*>(a.deltaT)), c.H, c.W, rows);
     }
-    if (c.z && c.softplus)
+    if (MODE == kModeVim && c.conv_w) {
+        if (c.z && c.softplus)
+            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, true, true>), grid, blk, 0, st, a);
+        else if (c.z)
+            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, false, true>), grid, blk, 0, st, a);
+        else if (c.softplus)
+            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, true>), grid, blk, 0, st, a);
+        else
+            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, true>), grid, blk, 0, st, a);
+    } else if (c.z && c.softplus)
         hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, true>), grid, blk, 0, st, a);
     else if (c.z)
         hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, false>), grid, blk, 0, st, a);
@@ -719,6 +758,23 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    void* stream) {
     Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
            A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    return run(c);
+}
+
+int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* x, const float* conv_w, const float* conv_b,
+                        const void* delta, const void* z, const void* B, const void* C,
+                        const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (!conv_w) {
+        g_last_error = "conv_w must not be NULL";
+        return VS_ERR_NULL;
+    }
+    Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, x, delta, z, B, C,
+           A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    c.conv_w = conv_w;
+    c.conv_b = conv_b;
     return run(c);
 }
 

@@ -88,6 +88,42 @@ def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplu
     return y
 
 
+def vim_scan_bidir_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip=None, dt_bias=None,
+                        delta_softplus=True, out=None, workspace=None):
+    """vim_scan_bidir with the Vim block's conv front end fused in: each
+    branch scans u_k = silu(conv_k(x)) (depthwise kernel 3, padding 1; the
+    backward branch on the flipped sequence).
+
+    x: [batch, dim, L]; conv_w: [2, dim, 3] fp32; conv_b: [2, dim] fp32 or
+    None; the rest as for vim_scan_bidir.
+    """
+    batch, dim, L = x.shape
+    dstate = A.shape[-1]
+    dt, dev = x.dtype, x.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("x", x), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("conv_w", conv_w, (2, dim, 3), dev, optional=False)
+    _param("conv_b", conv_b, (2, dim), dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    y = torch.empty_like(x) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir_conv(batch, dim, dstate, L, _DTYPES[dt], _ptr(x), _ptr(conv_w),
+                                     _ptr(conv_b), _ptr(delta), _ptr(z), _ptr(B), _ptr(C),
+                                     _ptr(A), _ptr(Dskip), _ptr(dt_bias),
+                                     int(bool(delta_softplus)), _ptr(y), _ptr(ws), ws_bytes,
+                                     _stream(dev))
+    nat.check("vim_scan_bidir_conv", rc)
+    return y
+
+
 def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
                        delta_softplus=True, out=None, workspace=None):
     """VMamba four-direction cross-scan of an H x W grid.
