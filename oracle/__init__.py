@@ -57,6 +57,8 @@ def _bind(lib):
     lib.oracle_scan_ex_f64.restype = I
     lib.oracle_vim_conv_f64.argtypes = [I, I, I, Lg, P, P, P, P, P, P, P, P, P, P, I, P, I]
     lib.oracle_vim_conv_f64.restype = I
+    lib.oracle_vim_bidir_grad_f64.argtypes = [I, I, I, Lg] + [P] * 8 + [I] + [P] * 9 + [I]
+    lib.oracle_vim_bidir_grad_f64.restype = I
     return lib
 
 
@@ -141,6 +143,35 @@ def vim_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip, dt_bias, delta_softplu
     if rc != 0:
         raise ValueError("oracle_vim_conv_f64 failed with status %d" % rc)
     return y
+
+
+GRAD_NAMES = ("du", "ddelta", "dz", "dB", "dC", "dA", "dD", "ddt_bias")
+
+
+def vim_bidir_grad(u, delta, z, B, C, A, Dskip, dt_bias, g, delta_softplus=True, nthreads=None,
+                   lib=None):
+    """Gradient of vim_bidir's output against an upstream gradient g (same
+    shape as y). Returns a dict: du, ddelta, dz [batch, dim, L]; dB, dC
+    [batch, dstate, L]; dA [2, dim, dstate]; dD, ddt_bias [2, dim] (dz is 0
+    without a gate)."""
+    lib = lib or load()
+    u, delta, z, B, C, A, g = map(_f64, (u, delta, z, B, C, A, g))
+    Dskip, dt_bias = _f64(Dskip), _f64(dt_bias)
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    assert delta.shape == u.shape and g.shape == u.shape and (z is None or z.shape == u.shape)
+    assert A.shape == (2, dim, dstate) and B.shape == (batch, dstate, L) and C.shape == B.shape
+    out = {k: np.empty(u.shape) for k in ("du", "ddelta", "dz")}
+    out.update(dB=np.empty(B.shape), dC=np.empty(B.shape), dA=np.empty(A.shape),
+               dD=np.empty((2, dim)), ddt_bias=np.empty((2, dim)))
+    rc = lib.oracle_vim_bidir_grad_f64(batch, dim, dstate, L, _ptr(u), _ptr(delta), _ptr(z),
+                                       _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias),
+                                       int(bool(delta_softplus)), _ptr(g),
+                                       *[_ptr(out[k]) for k in GRAD_NAMES],
+                                       nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_vim_bidir_grad_f64 failed with status %d" % rc)
+    return out
 
 
 def cross4(u, delta, z, B, C, A, Dskip, dt_bias, H, W, delta_softplus=True, nthreads=None):

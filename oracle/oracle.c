@@ -304,3 +304,200 @@ int oracle_s6_1d_f64(int batch, int dim, int dstate, long L, int reverse, const 
     return oracle_scan_f64(batch, dim, dstate, L, 0, 0, 1, order, u, delta, z, B, C, 0,
                            A, Dskip, dt_bias, delta_softplus, y, nthreads);
 }
+
+/* ------------------------------------------------------------------------
+ * Gradient of the Vim scan (oracle_vim_bidir_f64) with respect to every
+ * input, for an upstream gradient g of y. Reverse-mode differentiation of
+ * the definition above, per direction k in its own step order t
+ * (p = token visited at step t, q = the B/C entry of that step):
+ *   out[p]  = s[p] * silu(z[p]),  s[p] = sum_k y_k[p]
+ *   gs[p]   = g[p] * silu(z[p]);  dz[p] = g[p] * s[p] * silu'(z[p])
+ *   lam_t   = gs[p] C_t + e_{t+1} lam_{t+1}        (lam after the last step = 0)
+ *   dC_t   += gs[p] h_t;  dB_t += lam_t * delta_t * u[p]
+ *   du[p]  += gs[p] D_k + sum_n lam_t delta_t B_t
+ *   ddelta_t = sum_n lam_t (h_{t-1} e_t A + B_t u[p])
+ *   dA_k   += lam_t h_{t-1} e_t delta_t;  dD_k += gs[p] u[p]
+ *   dx_t    = ddelta_t * sigmoid(x_t) (softplus' ; 1 without softplus),
+ *             x_t = delta_raw[p] + dt_bias_k
+ *   ddelta_raw[p] += dx_t;  ddt_bias_k += dx_t
+ * with e_t = exp(delta_t A) and h the forward states (kept per unit).
+ * B and C are shared by every channel, so dB and dC sum over channels and
+ * directions; A, D and dt_bias sum over batch rows.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int batch, dim, dstate;
+    long L;
+    const double *u, *delta, *z, *B, *C, *A, *Dskip, *dt_bias, *g;
+    int delta_softplus;
+    double *du, *ddelta, *dz;                 /* [batch][dim][L], written per unit */
+    double *dB, *dC;                          /* [batch][dstate][L], this thread's sums */
+    double *dA, *dD, *dbias;                  /* [2][dim][dstate], [2][dim], this thread's sums */
+    long unit_begin, unit_end;
+} grad_job_t;
+
+static double sigmoid(double x)
+{
+    return x >= 0.0 ? 1.0 / (1.0 + exp(-x)) : exp(x) / (1.0 + exp(x));
+}
+
+static int grad_unit(const grad_job_t* J, long unit)
+{
+    const long b = unit / J->dim, d = unit % J->dim;
+    const long L = J->L, N = J->dstate, row = (b * J->dim + d) * L;
+    const double *u = J->u + row, *dl = J->delta + row, *g = J->g + row;
+    const double *Bb = J->B + b * N * L, *Cb = J->C + b * N * L;
+    double *du = J->du + row, *ddl = J->ddelta + row, *dz = J->dz + row;
+    double *dBb = J->dB + b * N * L, *dCb = J->dC + b * N * L;
+    /* forward states h_t (both directions) and deltas, kept for the reverse pass */
+    double* hs = (double*)malloc(sizeof(double) * (size_t)(2 * L * N));
+    double* dts = (double*)malloc(sizeof(double) * (size_t)(2 * L));
+    double* s = (double*)malloc(sizeof(double) * (size_t)L);
+    double* gs = (double*)malloc(sizeof(double) * (size_t)L);
+    double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!hs || !dts || !s || !gs || !lam) {
+        free(hs); free(dts); free(s); free(gs); free(lam);
+        return -2;
+    }
+    for (long p = 0; p < L; ++p) s[p] = 0.0;
+    for (int k = 0; k < 2; ++k) {
+        const double* A = J->A + ((long)k * J->dim + d) * N;
+        const double Dk = J->Dskip ? J->Dskip[(long)k * J->dim + d] : 0.0;
+        const double bias = J->dt_bias ? J->dt_bias[(long)k * J->dim + d] : 0.0;
+        double* h = hs + (long)k * L * N;
+        for (long t = 0; t < L; ++t) {
+            const long p = k == 0 ? t : L - 1 - t;
+            const double x = dl[p] + bias;
+            const double delta = J->delta_softplus ? softplus(x) : x;
+            dts[(long)k * L + t] = delta;
+            double yk = Dk * u[p];
+            for (long n = 0; n < N; ++n) {
+                const double prev = t > 0 ? h[(t - 1) * N + n] : 0.0;
+                h[t * N + n] = exp(delta * A[n]) * prev + delta * Bb[n * L + p] * u[p];
+                yk += Cb[n * L + p] * h[t * N + n];
+            }
+            s[p] += yk;
+        }
+    }
+    /* gate */
+    for (long p = 0; p < L; ++p) {
+        if (J->z) {
+            const double zz = J->z[row + p], sg = sigmoid(zz);
+            gs[p] = g[p] * zz * sg;
+            dz[p] = g[p] * s[p] * sg * (1.0 + zz * (1.0 - sg));
+        } else {
+            gs[p] = g[p];
+            dz[p] = 0.0;
+        }
+        du[p] = 0.0;
+        ddl[p] = 0.0;
+    }
+    /* reverse pass, per direction */
+    for (int k = 0; k < 2; ++k) {
+        const double* A = J->A + ((long)k * J->dim + d) * N;
+        const double Dk = J->Dskip ? J->Dskip[(long)k * J->dim + d] : 0.0;
+        const double bias = J->dt_bias ? J->dt_bias[(long)k * J->dim + d] : 0.0;
+        const double* h = hs + (long)k * L * N;
+        double* dA = J->dA + ((long)k * J->dim + d) * N;
+        for (long n = 0; n < N; ++n) lam[n] = 0.0;
+        double next_delta = 0.0;                       /* delta_{t+1} */
+        for (long t = L - 1; t >= 0; --t) {
+            const long p = k == 0 ? t : L - 1 - t;
+            const double delta = dts[(long)k * L + t];
+            double ddelta = 0.0, dupart = 0.0;
+            for (long n = 0; n < N; ++n) {
+                const double e_next = t + 1 < L ? exp(next_delta * A[n]) : 0.0;
+                lam[n] = gs[p] * Cb[n * L + p] + e_next * lam[n];
+                const double hprev = t > 0 ? h[(t - 1) * N + n] : 0.0;
+                const double e = exp(delta * A[n]);
+                dCb[n * L + p] += gs[p] * h[t * N + n];
+                dBb[n * L + p] += lam[n] * delta * u[p];
+                dupart += lam[n] * delta * Bb[n * L + p];
+                ddelta += lam[n] * (hprev * e * A[n] + Bb[n * L + p] * u[p]);
+                dA[n] += lam[n] * hprev * e * delta;
+            }
+            du[p] += gs[p] * Dk + dupart;
+            if (J->dD) J->dD[(long)k * J->dim + d] += gs[p] * u[p];
+            const double x = dl[p] + bias;
+            const double dx = ddelta * (J->delta_softplus ? sigmoid(x) : 1.0);
+            ddl[p] += dx;
+            if (J->dbias) J->dbias[(long)k * J->dim + d] += dx;
+            next_delta = delta;
+        }
+    }
+    free(hs); free(dts); free(s); free(gs); free(lam);
+    return 0;
+}
+
+static void* grad_worker(void* arg)
+{
+    const grad_job_t* J = (const grad_job_t*)arg;
+    for (long unit = J->unit_begin; unit < J->unit_end; ++unit)
+        if (grad_unit(J, unit) != 0) return (void*)1;
+    return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
+ * Every output is overwritten. Dskip, dt_bias and z may be NULL (zeros / no
+ * gate); dD and dbias are then still returned (the gradient at 0). */
+int oracle_vim_bidir_grad_f64(int batch, int dim, int dstate, long L, const double* u,
+                              const double* delta, const double* z, const double* B,
+                              const double* C, const double* A, const double* Dskip,
+                              const double* dt_bias, int delta_softplus, const double* g,
+                              double* du, double* ddelta, double* dz, double* dB, double* dC,
+                              double* dA, double* dD, double* dbias, int nthreads)
+{
+    if (batch < 1 || dim < 1 || dstate < 1 || L < 1) return -1;
+    if (!u || !delta || !B || !C || !A || !g || !du || !ddelta || !dz || !dB || !dC || !dA ||
+        !dD || !dbias)
+        return -1;
+    const long units = (long)batch * dim;
+    const size_t nbc = (size_t)batch * dstate * L, na = (size_t)2 * dim * dstate,
+                 nd = (size_t)2 * dim;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > units) nthreads = (int)units;
+    grad_job_t* jobs = (grad_job_t*)calloc((size_t)nthreads, sizeof(grad_job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    /* per-thread sums of the shared gradients */
+    double* acc = (double*)calloc((size_t)nthreads * (2 * nbc + na + 2 * nd), sizeof(double));
+    if (!jobs || !th || !acc) { free(jobs); free(th); free(acc); return -2; }
+    for (int i = 0; i < nthreads; ++i) {
+        grad_job_t* J = &jobs[i];
+        double* a = acc + (size_t)i * (2 * nbc + na + 2 * nd);
+        J->batch = batch; J->dim = dim; J->dstate = dstate; J->L = L;
+        J->u = u; J->delta = delta; J->z = z; J->B = B; J->C = C; J->A = A;
+        J->Dskip = Dskip; J->dt_bias = dt_bias; J->g = g; J->delta_softplus = delta_softplus;
+        J->du = du; J->ddelta = ddelta; J->dz = dz;
+        J->dB = a; J->dC = a + nbc; J->dA = a + 2 * nbc; J->dD = a + 2 * nbc + na;
+        J->dbias = a + 2 * nbc + na + nd;
+        J->unit_begin = units * i / nthreads;
+        J->unit_end = units * (i + 1) / nthreads;
+    }
+    int rc = 0, started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, grad_worker, &jobs[i]) != 0) break;
+        started = i;
+    }
+    if (grad_worker(&jobs[0]) != NULL) rc = -2;
+    for (int i = 1; i <= started; ++i) {
+        void* r = NULL;
+        pthread_join(th[i], &r);
+        if (r != NULL) rc = -2;
+    }
+    for (int i = started + 1; i < nthreads; ++i)
+        if (grad_worker(&jobs[i]) != NULL) rc = -2;
+    /* sum the threads' shared gradients */
+    for (size_t j = 0; j < nbc; ++j) { dB[j] = 0.0; dC[j] = 0.0; }
+    for (size_t j = 0; j < na; ++j) dA[j] = 0.0;
+    for (size_t j = 0; j < nd; ++j) { dD[j] = 0.0; dbias[j] = 0.0; }
+    for (int i = 0; i < nthreads; ++i) {
+        const double* a = acc + (size_t)i * (2 * nbc + na + 2 * nd);
+        for (size_t j = 0; j < nbc; ++j) { dB[j] += a[j]; dC[j] += a[nbc + j]; }
+        for (size_t j = 0; j < na; ++j) dA[j] += a[2 * nbc + j];
+        for (size_t j = 0; j < nd; ++j) {
+            dD[j] += a[2 * nbc + na + j];
+            dbias[j] += a[2 * nbc + na + nd + j];
+        }
+    }
+    free(jobs); free(th); free(acc);
+    return rc;
+}
