@@ -366,13 +366,13 @@ static int grad_unit(const grad_job_t* J, long unit)
         double* h = hs + (long)k * L * N;
         for (long t = 0; t < L; ++t) {
             const long p = k == 0 ? t : L - 1 - t;
-            const double x = dl[p] + bias;
-            const double delta = J->delta_softplus ? softplus(x) : x;
+            const double x = bias + dl[p];
+            const double delta = !J->delta_softplus ? x : softplus(x);
             dts[(long)k * L + t] = delta;
             double yk = Dk * u[p];
             for (long n = 0; n < N; ++n) {
                 const double prev = t > 0 ? h[(t - 1) * N + n] : 0.0;
-                h[t * N + n] = exp(delta * A[n]) * prev + delta * Bb[n * L + p] * u[p];
+                h[t * N + n] = exp(A[n] * delta) * prev + delta * Bb[n * L + p] * u[p];
                 yk += Cb[n * L + p] * h[t * N + n];
             }
             s[p] += yk;
@@ -408,7 +408,7 @@ static int grad_unit(const grad_job_t* J, long unit)
                 const double e_next = t + 1 < L ? exp(next_delta * A[n]) : 0.0;
                 lam[n] = gs[p] * Cb[n * L + p] + e_next * lam[n];
                 const double hprev = t > 0 ? h[(t - 1) * N + n] : 0.0;
-                const double e = exp(delta * A[n]);
+                const double e = exp(A[n] * delta);
                 dCb[n * L + p] += gs[p] * h[t * N + n];
                 dBb[n * L + p] += lam[n] * delta * u[p];
                 dupart += lam[n] * delta * Bb[n * L + p];
@@ -417,7 +417,7 @@ static int grad_unit(const grad_job_t* J, long unit)
             }
             du[p] += gs[p] * Dk + dupart;
             if (J->dD) J->dD[(long)k * J->dim + d] += gs[p] * u[p];
-            const double x = dl[p] + bias;
+            const double x = bias + dl[p];
             const double dx = ddelta * (J->delta_softplus ? sigmoid(x) : 1.0);
             ddl[p] += dx;
             if (J->dbias) J->dbias[(long)k * J->dim + d] += dx;
