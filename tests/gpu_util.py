@@ -27,9 +27,20 @@ def half_ulp(ref, dtype):
 
 
 def strict_err(y, ref, dtype):
+    assert_finite(y, ref, "strict")
     rms = float(np.sqrt(np.mean(ref ** 2)))
     excess = np.abs(y - ref) - half_ulp(ref, dtype)
     return float(np.max(excess)) / rms, rms
+
+
+def stable_without_softplus(inp):
+    """Make delta_raw + dt_bias positive (0.2 |delta_raw| + 0.05), so that the
+    scan stays bounded when softplus is off; delta is re-rounded to the input
+    dtype so that both sides see the same values."""
+    d = np.abs(inp.delta) * np.float32(0.2)
+    inp.delta = wlm.round_bf16(d) if inp.wl.dtype == wlm.BF16 else d.astype(np.float32)
+    inp.dt_bias = np.full_like(inp.dt_bias, 0.05)
+    return inp
 
 
 def say(msg):
@@ -76,7 +87,17 @@ def rel_err(y, ref):
     return float(np.max(np.abs(y - ref) / (1.0 + np.abs(ref))))
 
 
+def assert_finite(y, ref, what=""):
+    """Both sides must be finite: comparisons with NaN are false, so a
+    non-finite result would otherwise pass every tolerance test."""
+    if not np.all(np.isfinite(ref)):
+        raise AssertionError("%s: the reference holds non-finite values" % what)
+    if not np.all(np.isfinite(y)):
+        raise AssertionError("%s: %d non-finite outputs" % (what, int(np.sum(~np.isfinite(y)))))
+
+
 def assert_close(y, ref, dtype, what=""):
+    assert_finite(y, ref, what)
     err = rel_err(y, ref)
     bad = np.abs(y - ref) > TOL[dtype] * (1.0 + np.abs(ref))
     if bad.any():

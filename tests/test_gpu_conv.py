@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import STRICT, assert_close, dev, host64, say, strict_err, torch_dtype, upload
+from gpu_util import (STRICT, assert_close, dev, host64, say, stable_without_softplus,
+                      strict_err, torch_dtype, upload)
 from vision_mamba_selective_amd import workloads as wlm
 
 pytestmark = pytest.mark.gpu
@@ -66,7 +67,7 @@ def test_conv_small(shape, base, bias):
 def test_conv_no_gate_no_softplus(base):
     wl = base.with_(batch=2, dim=11, seqlen=70, gate=False)
     inp = wlm.make_inputs(wl, random_D=True)
-    inp.delta = np.abs(inp.delta) * 0.2
+    stable_without_softplus(inp)
     w, cb = conv_params(11, seed=9)
     say("case conv no gate, softplus off")
     y = host64(run(inp, w, cb, delta_softplus=False))
