@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--conv", action="store_true",
                    help="time vim_scan_bidir_conv: the same scan with the Vim block's conv1d + "
                         "SiLU front end fused into its token loads (u is then the conv input x)")
+    p.add_argument("--grad", action="store_true",
+                   help="time vim_scan_bidir_grad: the reverse-mode gradient of the scan for a "
+                        "synthetic upstream gradient (forward recompute + adjoint pass)")
     p.add_argument("--copy-probe", action="store_true",
                    help="instead of the scan, run torch copies of known size (counter scale)")
     return p.parse_args()
@@ -89,8 +92,11 @@ def main():
 
     idx = wlm.HEADLINE if args.workload is None else args.workload
     wl = wlm.WORKLOADS[idx]
-    if args.conv and wl.kind != "vim":
-        print("--conv applies to the Vim workloads only", file=sys.stderr)
+    if (args.conv or args.grad) and wl.kind != "vim":
+        print("--conv and --grad apply to the Vim workloads only", file=sys.stderr)
+        sys.exit(2)
+    if args.conv and args.grad:
+        print("--conv and --grad are separate measurements", file=sys.stderr)
         sys.exit(2)
     tdt = torch.bfloat16 if wl.dtype == wlm.BF16 else torch.float32
     print("bench: workload %s" % wl.name, file=sys.stderr, flush=True)
@@ -106,6 +112,10 @@ def main():
     base = dict(u=up(inp.u, tdt), delta=up(inp.delta, tdt), z=up(inp.z, tdt), B=up(inp.B, tdt),
                 C=up(inp.C, tdt), A=up(inp.A, torch.float32), D=up(inp.D, torch.float32),
                 bias=up(inp.dt_bias, torch.float32))
+    if args.grad:
+        grng = np.random.default_rng(wl.seed + 600)
+        gy = grng.standard_normal(inp.u.shape).astype(np.float32)
+        base["dy"] = up(wlm.round_bf16(gy) if wl.dtype == wlm.BF16 else gy, tdt)
     if args.conv:
         crng = np.random.default_rng(wl.seed + 500)
         base["cw"] = up((0.6 * crng.standard_normal((2, wl.dim, 3))).astype(np.float32),
@@ -116,13 +126,38 @@ def main():
         t = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
         t["y"] = torch.empty_like(t["u"])
         t["ws"] = None
-        need = vms.workspace_bytes(0 if wl.kind == "vim" else 1, wl.batch, wl.dim, wl.seqlen, tdt)
+        op = 3 if args.grad else (0 if wl.kind == "vim" else 1)
+        need = vms.workspace_bytes(op, wl.batch, wl.dim, wl.seqlen, tdt)
         if need:
             t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
         sets.append(t)
 
+    if args.grad:
+        for t in sets:
+            t["g"] = dict(du=torch.empty_like(t["u"]), ddelta=torch.empty_like(t["u"]),
+                          dz=None if t["z"] is None else torch.empty_like(t["u"]),
+                          dB=torch.empty(wl.batch, wl.dstate, wl.seqlen, device=dev),
+                          dC=torch.empty(wl.batch, wl.dstate, wl.seqlen, device=dev),
+                          dA=torch.empty(2, wl.dim, wl.dstate, device=dev),
+                          dD=torch.empty(2, wl.dim, device=dev),
+                          db=torch.empty(2, wl.dim, device=dev))
+        from vision_mamba_selective_amd import _native as nat
+
+        def grad_call(t):
+            g = t["g"]
+            p = lambda x: None if x is None else x.data_ptr()
+            rc = nat.lib.vim_scan_bidir_grad(
+                wl.batch, wl.dim, wl.dstate, wl.seqlen, nat.VS_BF16 if wl.dtype == wlm.BF16
+                else nat.VS_F32, p(t["u"]), p(t["delta"]), p(t["z"]), p(t["B"]), p(t["C"]),
+                p(t["A"]), p(t["D"]), p(t["bias"]), 1, p(t["dy"]), p(g["du"]), p(g["ddelta"]),
+                p(g["dz"]), p(g["dB"]), p(g["dC"]), p(g["dA"]), p(g["dD"]), p(g["db"]),
+                p(t["ws"]), t["ws"].numel(), torch.cuda.current_stream(dev).cuda_stream)
+            nat.check("vim_scan_bidir_grad", rc)
+
     def step(t):
-        if args.conv:
+        if args.grad:
+            grad_call(t)
+        elif args.conv:
             vms.vim_scan_bidir_conv(t["u"], t["cw"], t["cb"], t["delta"], t["z"], t["B"], t["C"],
                                     t["A"], t["D"], t["bias"], out=t["y"], workspace=t["ws"])
         elif wl.kind == "vim":
@@ -165,7 +200,7 @@ def main():
         try:
             with open(PROFILE_TRAFFIC) as f:
                 tr = json.load(f)
-            rec = tr.get(wl.name + ("+conv" if args.conv else ""))
+            rec = tr.get(wl.name + ("+conv" if args.conv else "") + ("+grad" if args.grad else ""))
             if rec and rec.get("kernel_sha") == kernel_hash():
                 traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -187,7 +222,8 @@ def main():
         "config": {"workload": wl.name, "kind": wl.kind, "batch": wl.batch, "d_inner": wl.dim,
                    "d_state": wl.dstate, "seq_len": wl.seqlen, "directions": wl.ndir,
                    "state_dtype": "f32", "input_sets_rotated": nsets,
-                   "front_end": "conv1d k3 + silu, fused" if args.conv else "none"},
+                   "front_end": "conv1d k3 + silu, fused" if args.conv else "none",
+                   "pass": "gradient (forward recompute + adjoint)" if args.grad else "forward"},
         "hbm_GBps": round(hbm_gbs, 1),
         "kernel_ms": round(kern_avg_s * 1e3, 5),
         "roofline": {
@@ -211,12 +247,14 @@ def main():
         conv = None
         if args.conv:
             conv = (base["cw"].cpu().numpy(), base["cb"].cpu().numpy())
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv,
+                                           base["dy"].float().cpu().numpy() if args.grad else None)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, nch, conv=None):
+def cpu_baseline(wl, inp, nch, conv=None, dy=None):
     """The fp64 oracle, as it stands, on the host cores of this machine."""
+    import numpy as np
     import oracle
     from vision_mamba_selective_amd import workloads as wlm
 
@@ -230,7 +268,12 @@ def cpu_baseline(wl, inp, nch, conv=None):
           flush=True)
     oracle.load()
     t0 = time.perf_counter()
-    if conv is None:
+    if dy is not None:
+        gy = dy[:sample.wl.batch, :sample.wl.dim]
+        oracle.vim_bidir_grad(sample.u, sample.delta, sample.z, sample.B, sample.C, sample.A,
+                              sample.D, sample.dt_bias, np.ascontiguousarray(gy),
+                              nthreads=threads)
+    elif conv is None:
         oracle.run_inputs(sample, nthreads=threads)
     else:
         w, b = conv

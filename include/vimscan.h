@@ -74,12 +74,14 @@ enum {
 };
 
 /* operation kinds for vs_workspace_bytes */
-enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2 };
+enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 };
 
 /* Largest supported state size (the pages use 16 by default and 8 in a test). */
 #define VS_MAX_DSTATE 16
 
-/* Bytes of device workspace an operation needs, in units of E =
+/* Bytes of device workspace an operation needs (VS_OP_VIM_GRAD: the
+ * gradient's forward output, per-block states and partial sums, about
+ * 20 bytes per element). Otherwise, in units of E =
  * batch*dim*seqlen elements. Direction merge: fp32 buffers of E floats,
  * one for VS_OP_VIM_BIDIR and two for VS_OP_CROSS4 (one per pair of opposite
  * directions); an fp32 y serves as the first, so fp32 needs one fewer.
@@ -133,6 +135,37 @@ int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         const float* A, const float* Dskip, const float* dt_bias,
                         int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * Gradient of vim_scan_bidir (reverse mode) for an upstream gradient dy of
+ * y: the derivative of the definition at the top of this file with respect
+ * to every input, differentiated step by step (the adjoint of the state,
+ * lam_t = dy_t silu(z_t) C_t + e_{t+1} lam_{t+1}, runs backwards over each
+ * direction's steps over states recomputed from the forward pass). It is
+ * the backward half of a training step on the guide's Vim block (section
+ * "2. The Bidirectional Mamba Block"); the pages themselves stop at the
+ * forward pass.
+ *   inputs         as for vim_scan_bidir (same layouts, dtype and meaning)
+ *   dy             [batch][dim][L], dtype: dL/dy
+ *   du, ddelta     [batch][dim][L], dtype: dL/du, dL/d delta_raw
+ *   dz             [batch][dim][L], dtype; required when z is given, not
+ *                  used (may be NULL) otherwise
+ *   dB, dC         [batch][dstate][L] fp32, summed over channels and both
+ *                  directions
+ *   dA             [2][dim][dstate] fp32; dD, ddt_bias [2][dim] fp32 (summed
+ *                  over batch rows); returned even when Dskip / dt_bias are
+ *                  NULL (the gradient at 0)
+ *   workspace      at least vs_workspace_bytes(VS_OP_VIM_GRAD, ...) bytes
+ * Every output is overwritten. dB, dC, dA, dD and ddt_bias are sums of fp32
+ * atomic additions, so their last bits may differ between calls. No output
+ * may overlap an input, another output or the workspace (VS_ERR_ALIAS).
+ */
+int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* u, const void* delta, const void* z, const void* B,
+                        const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, const void* dy, void* du, void* ddelta, void* dz,
+                        float* dB, float* dC, float* dA, float* dD, float* ddt_bias,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * VMamba four-direction cross-scan of an H x W grid (L = H*W tokens, stored

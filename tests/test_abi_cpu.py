@@ -25,7 +25,8 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for required in ("vim_scan_bidir", "vim_scan_bidir_conv", "vmamba_cross_scan4",
+    for required in ("vim_scan_bidir", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
+                     "vmamba_cross_scan4",
                      "s6_scan_1d", "vs_strerror",
                      "vs_last_error", "vs_abi_version", "vs_workspace_bytes"):
         assert required in names
@@ -144,6 +145,28 @@ def test_conv_validation(nat):
     assert call(b=fake(11) + 1) == -4
     assert call(y=fake(10) - 64) == -5          # y runs into conv_w
     assert call(x=None) == -1
+
+
+def test_grad_validation(nat):
+    f = nat.lib.vim_scan_bidir_grad
+    need = nat.lib.vs_workspace_bytes(3, 2, 8, 33, nat.VS_BF16)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(u=fake(0), dl=fake(1), z=fake(2), B=fake(3), C=fake(4), A=fake(5), D=None,
+                 bias=None, dy=fake(6), du=fake(7), dd=fake(8), dz=fake(9), dB=fake(10),
+                 dC=fake(11), dA=fake(12), dD=fake(13), db=fake(14), ws=fake(15), wsb=need)
+        a.update(kw)
+        return f(2, 8, 16, 33, nat.VS_BF16, a["u"], a["dl"], a["z"], a["B"], a["C"], a["A"],
+                 a["D"], a["bias"], 1, a["dy"], a["du"], a["dd"], a["dz"], a["dB"], a["dC"],
+                 a["dA"], a["dD"], a["db"], a["ws"], a["wsb"], None)
+    assert call(dy=None) == -1
+    assert call(dB=None) == -1
+    assert call(dz=None) == -1                   # z given: dz required
+    assert call(wsb=need - 1) == -8
+    assert call(du=fake(0) + 64) == -5           # du inside u
+    assert call(dC=fake(10) + 128) == -5         # dC overlaps dB
+    assert call(dA=fake(12) + 2) == -4
 
 
 def test_1d_validation(nat):

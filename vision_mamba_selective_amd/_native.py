@@ -14,7 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libvimscan.so")
 
 VS_F32, VS_BF16 = 0, 1
-VS_OP_VIM_BIDIR, VS_OP_CROSS4, VS_OP_1D = 0, 1, 2
+VS_OP_VIM_BIDIR, VS_OP_CROSS4, VS_OP_1D, VS_OP_VIM_GRAD = 0, 1, 2, 3
 
 # names and argument types of every entry point declared in include/vimscan.h
 _I64 = ctypes.c_int64
@@ -27,6 +27,8 @@ SIGNATURES = {
                             _P, _P, _SZ, _P]),
     "vim_scan_bidir_conv": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _I, _P, _P, _SZ, _P]),
+    "vim_scan_bidir_grad": (_I, [_I64, _I64, _I64, _I64, _I] + [_P] * 8 + [_I] + [_P] * 9 +
+                            [_P, _SZ, _P]),
     "vmamba_cross_scan4": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _I, _P, _P, _SZ, _P]),
     "s6_scan_1d": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,

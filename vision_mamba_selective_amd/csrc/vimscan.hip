@@ -63,6 +63,7 @@ struct ScanArgs {
     float* partial2;    // cross-scan: the column-major pair's partial sums
     const void* uT;     // cross-scan: u and delta transposed to column-major
     const void* deltaT;
+    float* ckpt;            // gradient recompute: state at each block start
     const float* conv_w;    // Vim front end: depthwise taps [2][dim][3] (u holds x)
     const float* conv_b;    // and biases [2][dim] (NULL: 0)
     int64_t dim;
@@ -235,9 +236,13 @@ struct Unroll<0> {
 // sums are read only after it. Vim finishes a token by gating and storing
 // y; the cross-scan stores the pair's sum, and after the loop the workgroup
 // adds its two pairs' sums, gates and stores y.
-template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false>
+template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
+    // CKPT (the gradient's forward pass): store every row's state at each
+    // block start and, in place of y, the merged ungated sum in the partial
+    // buffer (fp32)
+    static_assert(!CKPT || (MODE == kModeVim && !GATE), "checkpoints: ungated Vim only");
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
@@ -393,6 +398,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     float h = 0.f;
+    float* ck_row = nullptr;
+    if (CKPT)
+        ck_row = a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
     // One block step. `cur` holds this block's token data (loaded one step
     // earlier), `nxt` receives the next block's; the loop below alternates
     // the two so that no register of an in-flight load is ever copied.
@@ -400,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int buf = blk & 1;
         const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
+        if (CKPT && active) ck_row[blk * kRowLanes + n] = h;
         // the other direction's partial sum, for blocks after step F (it was
         // stored at step F or earlier, before F's fence); earlier blocks load
         // entry 0 of the row instead (unused) rather than branch. Issued
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // a token's second visit: Vim gates and stores y, the cross-scan
         // stores the pair's fp32 sum
         auto finish = [&](float sum) {
-            if (MODE == kModeCross4) *part_at(p) = sum;
+            if (MODE == kModeCross4 || CKPT) *part_at(p) = sum;
             else st(y_at(p), 0, sum * gate);
         };
 
@@ -538,6 +547,310 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             }
         }
     }
+}
+
+// ---------------------------------------------------------------- gradient
+// Reverse-mode gradient of the Vim scan (vim_scan_bidir_grad). Same row
+// layout as rowscan_kernel (one recurrence per 16-lane row, lane n = state
+// n, 8 channels x {forward, backward} per workgroup) with the blocks taken
+// in reverse order. Per block:
+//   * the states h_t of the block's 16 steps are recomputed from the state
+//     stored at the block's start by the forward pass (rowscan_kernel with
+//     CKPT), keeping h_t and e_t = exp(delta_t A_n) in registers;
+//   * the adjoint runs backwards over the 16 steps,
+//       lam_t = gs_t C_t + e_{t+1} lam_{t+1},  gs = dy * silu(z),
+//     with lam and e_{t+1} carried across blocks;
+//   * per step and state: q = lam h_{t-1} e_t, dA += q delta_t,
+//     dC_t = gs_t h_t, dB_t = lam_t delta_t u_t; the sums over states
+//     R_w = sum_n lam B_t and R_v = sum_n q A_n are row transpose
+//     reductions (lane j ends with step j's sums), giving
+//       du_t = delta_t R_w + gs_t D,  ddelta_t = R_v + u_t R_w,
+//       ddelta_raw = ddelta_t * softplus'(x_t) = ddelta_t * sigmoid(x_t);
+//   * du and ddelta of the two directions merge through fp32 partial sums
+//     as the forward merge does (blocks above F hold first visits, below F
+//     second visits, block F is mixed);
+//   * dB and dC (shared by every channel) are summed over the workgroup's
+//     rows in LDS and added to global memory with fp32 atomics; dA, dD and
+//     dt_bias are summed per row and added once at the end.
+struct GradArgs {
+    const void *u, *delta, *z, *B, *C, *dy;
+    const float *A, *Dskip, *dt_bias;
+    const float* s;         // merged ungated forward output (fp32)
+    const float* ckpt;      // state at each block start, per row
+    float *pdu, *pdd;       // fp32 partial sums of du and ddelta_raw
+    void *du, *ddelta, *dz;
+    float *dB, *dC, *dA, *dD, *dbias;
+    int64_t dim, L;
+    int dstate, nblk;
+};
+
+__device__ __forceinline__ float sigmoid_f(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+template <typename T, bool GATE, bool SOFTPLUS>
+__global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
+    constexpr int kChPerWg = 8;
+    __shared__ __attribute__((aligned(16))) float tile[2][2][2][kRowLanes][kTilePad];
+    __shared__ float gbc[2][2][kRowLanes][kBlockTok];    // [side][dB|dC][n][step]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWaveLanes - 1);
+    const int row_in_wg = tid >> 4;
+    const int n = lane & (kRowLanes - 1);
+    const int dir = row_in_wg & 1;
+    const int ch = row_in_wg >> 1;
+    uint32_t cg, bb;
+    xcd_block(cg, bb);
+    const int64_t b = bb;
+    const int64_t d0 = static_cast<int64_t>(cg) * kChPerWg + ch;
+    const bool active = d0 < a.dim;
+    const int64_t d = active ? d0 : 0;
+    const int L = static_cast<int>(a.L);
+    const int nblk = a.nblk;
+    const bool rev = dir == 1;
+    const int64_t prow = dir * a.dim + d;
+    const bool n_ok = active && n < a.dstate;
+    const float An = n_ok ? a.A[prow * a.dstate + n] : 0.f;
+    const float A2 = An * kLog2e;
+    const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
+    const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
+
+    constexpr uint32_t kEs = sizeof(T);
+    const uint32_t rowoff = static_cast<uint32_t>((b * a.dim + d) * a.L);
+    const char* __restrict__ ub = static_cast<const char*>(a.u);
+    const char* __restrict__ db = static_cast<const char*>(a.delta);
+    const char* __restrict__ zb = static_cast<const char*>(a.z);
+    const char* __restrict__ gb = static_cast<const char*>(a.dy);
+    const char* __restrict__ sb = reinterpret_cast<const char*>(a.s);
+    auto act_at = [&](const char* base, int p) {
+        return ld_raw(reinterpret_cast<const T*>(base + (rowoff + static_cast<uint32_t>(p)) * kEs), 0);
+    };
+    auto f32_at = [&](const char* base, int p) {
+        return reinterpret_cast<const float*>(base + (rowoff + static_cast<uint32_t>(p)) * 4u);
+    };
+    auto out_at = [&](void* base, int p) {
+        return reinterpret_cast<T*>(static_cast<char*>(base) + (rowoff + static_cast<uint32_t>(p)) * kEs);
+    };
+    float* const pdu = a.pdu + rowoff;
+    float* const pdd = a.pdd + rowoff;
+    const float* const ck_row =
+        a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
+
+    // ---- B/C staging (as rowscan_kernel: side 0 reads token t, side 1 L-1-t)
+    constexpr int kStage = 4;
+    const int sn = tid >> 4, slot = tid & 15;
+    const bool sn_ok = sn < a.dstate;
+    const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
+    const char* __restrict__ Bb = static_cast<const char*>(a.B);
+    const char* __restrict__ Cb = static_cast<const char*>(a.C);
+    auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
+        const int t = blk * kBlockTok + slot;
+        const int tc = t < L ? t : L - 1;
+#pragma unroll
+        for (int r = 0; r < kStage; ++r) {
+            const uint32_t off = (bc_row + static_cast<uint32_t>((r >> 1) ? L - 1 - tc : tc)) * kEs;
+            sr[r] = ld_raw(reinterpret_cast<const T*>(((r & 1) ? Cb : Bb) + off), 0);
+        }
+    };
+    const int st_col = sn_ok ? slot : kRowLanes;
+    auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) {
+#pragma unroll
+        for (int r = 0; r < kStage; ++r)
+            tile[buf][r >> 1][r & 1][sn][st_col] = from_raw<T>(sr[r]);
+    };
+    if (!sn_ok) {
+#pragma unroll
+        for (int r = 0; r < kStage; ++r) {
+            tile[0][r >> 1][r & 1][sn][slot] = 0.f;
+            tile[1][r >> 1][r & 1][sn][slot] = 0.f;
+        }
+    }
+    // dB/dC accumulators: thread tid owns entries 4 tid .. 4 tid + 3
+    float* const gflat = &gbc[0][0][0][0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gflat[4 * tid + e] = 0.f;
+
+    auto tok_pos = [&](int blk) {
+        const int t = blk * kBlockTok + n;
+        const int tc = t < L ? t : L - 1;
+        return rev ? L - 1 - tc : tc;
+    };
+    const int Fstep = (L - 1) / (2 * kBlockTok);
+    struct Tok { uint32_t u, dl, z, g; float s; int p; };
+    auto tok_load = [&](int blk, Tok& k) {
+        const int p = tok_pos(blk);
+        k.p = p;
+        k.u = act_at(ub, p);
+        k.dl = act_at(db, p);
+        k.g = act_at(gb, p);
+        if (GATE) {
+            k.z = act_at(zb, p);
+            k.s = *f32_at(sb, dir == 0 ? p : 0);   // dz is written by the forward row
+        }
+    };
+
+    uint32_t sr[kStage];
+    const int last = nblk - 1;
+    stage_load(last, sr);
+    stage_store(last & 1, sr);
+    Tok tA{}, tB{};
+    tok_load(last, tA);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    float lam = 0.f, e_carry = 0.f, dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
+    auto step = [&](const int blk, Tok& cur, Tok& nxt) {
+        const int buf = blk & 1;
+        const int p = cur.p;
+        const bool ok = active && blk * kBlockTok + n < L;
+        // partial sums of the other direction's first visits (blocks below F)
+        float part_du = 0.f, part_dd = 0.f;
+        {
+            const int pp = blk < Fstep ? p : 0;
+            part_du = __hip_atomic_load(pdu + pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            part_dd = __hip_atomic_load(pdd + pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const int nb = blk > 0 ? blk - 1 : 0;
+        stage_load(nb, sr);
+        tok_load(nb, nxt);
+
+        // this lane's step (slot n) quantities
+        const float cu = from_raw<T>(cur.u);
+        const float x = from_raw<T>(cur.dl) + bias;
+        const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
+        const float du_ = dlt * cu;
+        const float g = from_raw<T>(cur.g);
+        float gs = g;
+        if (GATE) {
+            const float zz = from_raw<T>(cur.z);
+            const float sg = sigmoid_f(zz);
+            gs = g * zz * sg;
+            if (dir == 0 && ok)
+                st(out_at(a.dz, p), 0, g * cur.s * sg * fmaf(zz, 1.f - sg, 1.f));
+        }
+        gs = ok ? gs : 0.f;
+
+        const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][dir][0][n][0]);
+        const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][dir][1][n][0]);
+        float Bv[16], Cv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 bq = Bt[q], cq = Ct[q];
+            Bv[4 * q] = bq.x; Bv[4 * q + 1] = bq.y; Bv[4 * q + 2] = bq.z; Bv[4 * q + 3] = bq.w;
+            Cv[4 * q] = cq.x; Cv[4 * q + 1] = cq.y; Cv[4 * q + 2] = cq.z; Cv[4 * q + 3] = cq.w;
+        }
+        // recompute the block's states from the stored start state
+        const float h_in = active ? ck_row[blk * kRowLanes + n] : 0.f;
+        float hs[16], es[16];
+        {
+            float h = h_in;
+            Unroll<16>::run([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                es[i] = __builtin_amdgcn_exp2f(row_bcast<i>(dlt) * A2);
+                h = fmaf(es[i], h, row_bcast<i>(du_) * Bv[i]);
+                hs[i] = h;
+            });
+        }
+        // adjoint, backwards over the block's steps
+        float wv[16], vv[16];
+        Unroll<16>::run([&](auto ic) {
+            constexpr int i = 15 - decltype(ic)::value;
+            const float e_next = i < 15 ? es[i < 15 ? i + 1 : 15] : e_carry;
+            const float g_i = row_bcast<i>(gs);
+            lam = fmaf(e_next, lam, g_i * Cv[i]);
+            const float hprev = i > 0 ? hs[i > 0 ? i - 1 : 0] : h_in;
+            const float q = lam * hprev * es[i];
+            dA_acc = fmaf(q, row_bcast<i>(dlt), dA_acc);
+            wv[i] = lam * Bv[i];
+            vv[i] = q * An;
+            atomicAdd(&gbc[dir][1][n][i], g_i * hs[i]);
+            atomicAdd(&gbc[dir][0][n][i], lam * row_bcast<i>(du_));
+        });
+        e_carry = es[0];
+        const float Rw = row_transpose_sum(wv, lane);
+        const float Rv = row_transpose_sum(vv, lane);
+        const float du_tok = fmaf(dlt, Rw, gs * Dk);
+        const float ddl = fmaf(cu, Rw, Rv);
+        const float dx = SOFTPLUS ? ddl * sigmoid_f(x) : ddl;
+        if (ok) {
+            dbias_acc += dx;
+            dD_acc = fmaf(gs, cu, dD_acc);
+        }
+        // merge the two directions' du and ddelta_raw for this step's token
+        auto finish = [&](float vdu, float vdd) {
+            st(out_at(a.du, p), 0, vdu);
+            st(out_at(a.ddelta, p), 0, vdd);
+        };
+        if (blk > Fstep) {
+            if (ok) { pdu[p] = du_tok; pdd[p] = dx; }
+        } else if (blk < Fstep) {
+            if (ok) finish(du_tok + part_du, dx + part_dd);
+        } else {
+            const int t_self = blk * kBlockTok + n;
+            const int blk_other = (L - 1 - t_self) / kBlockTok;
+            const bool first = blk > blk_other || (blk == blk_other && dir == 0);
+            if (ok && first) {
+                __hip_atomic_store(pdu + p, du_tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(pdd + p, dx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            if (ok && !first) {
+                const float odu = __hip_atomic_load(pdu + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float odd = __hip_atomic_load(pdd + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                finish(du_tok + odu, dx + odd);
+            }
+        }
+
+        // every row's dB/dC of this block are in gbc: add them to global
+        // memory, clear, and stage the next block's B/C
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = 4 * tid + e;                  // [side][dB|dC][n][i]
+            const int side = idx >> 9, which = (idx >> 8) & 1, sn2 = (idx >> 4) & 15, i = idx & 15;
+            const int t = blk * kBlockTok + i;
+            const float v = gflat[idx];
+            gflat[idx] = 0.f;
+            if (t < L && sn2 < a.dstate) {
+                const int tk = side ? L - 1 - t : t;
+                float* dst = (which ? a.dC : a.dB) + (b * a.dstate + sn2) * a.L + tk;
+                atomicAdd(dst, v);
+            }
+        }
+        stage_store(buf ^ 1, sr);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    int blk = last;
+    for (; blk > 0; blk -= 2) {
+        step(blk, tA, tB);
+        step(blk - 1, tB, tA);
+    }
+    if (blk == 0) step(0, tA, tB);
+
+    // per-row sums: dA (lane n), dD and dt_bias (summed over the row's lanes)
+    if (n_ok) atomicAdd(&a.dA[prow * a.dstate + n], dA_acc);
+    float sD = dD_acc, sb2 = dbias_acc;
+    sD += dpp<0x4e>(sD); sb2 += dpp<0x4e>(sb2);              // quad_perm [2,3,0,1]
+    sD += dpp<0xb1>(sD); sb2 += dpp<0xb1>(sb2);              // quad_perm [1,0,3,2]
+    sD += dpp<0x114>(sD); sb2 += dpp<0x114>(sb2);            // row_shr:4 (lane 15: + lane 11)
+    sD += dpp<0x118>(sD); sb2 += dpp<0x118>(sb2);            // row_shr:8 (lane 15: + lane 7)
+    if (active && n == 15) {
+        atomicAdd(&a.dD[prow], sD);
+        atomicAdd(&a.dbias[prow], sb2);
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * kThreads)
+        p[i] = 0.f;
 }
 
 // Transpose u and delta of every (batch, channel) from the row-major H x W
@@ -719,6 +1032,140 @@ int launch_t(const Call& c) {
     return VS_OK;
 }
 
+// ---- gradient of the Vim scan
+struct GradCall {
+    int64_t batch, dim, dstate, L;
+    int dtype;
+    const void *u, *delta, *z, *B, *C;
+    const float *A, *Dskip, *dt_bias;
+    int softplus;
+    const void* dy;
+    void *du, *ddelta, *dz;
+    float *dB, *dC, *dA, *dD, *dbias;
+    void* ws;
+    size_t ws_bytes;
+    void* stream;
+};
+
+// workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
+// [du partials: fp32 E][ddelta partials: fp32 E], each 256-byte aligned
+size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[4]) {
+    const size_t elems = static_cast<size_t>(batch * dim * L);
+    const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
+    const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
+    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    size_t off = 0;
+    offs[0] = off; off += al(4 * elems);
+    offs[1] = off; off += al(4 * ck);
+    offs[2] = off; off += al(4 * elems);
+    offs[3] = off; off += al(4 * elems);
+    return off;
+}
+
+int validate_grad(const GradCall& g) {
+    if (g.dtype != VS_F32 && g.dtype != VS_BF16) return fail(VS_ERR_DTYPE, "unknown dtype");
+    if (g.batch < 1 || g.dim < 1 || g.L < 1 || g.dstate < 1)
+        return fail(VS_ERR_SHAPE, "batch, dim, dstate and the sequence length must be >= 1");
+    if (g.dstate > VS_MAX_DSTATE)
+        return fail(VS_ERR_UNSUPPORTED, "dstate above 16 is not supported");
+    if (g.batch > 65535) return fail(VS_ERR_SHAPE, "batch above 65535 is not supported");
+    if (g.L > (int64_t(1) << 30) || g.dim > (int64_t(1) << 30))
+        return fail(VS_ERR_SHAPE, "sequence length or dim too large");
+    const int64_t elems = g.batch * g.dim * g.L;
+    if (elems >= (int64_t(1) << 30) || g.batch * g.dstate * g.L >= (int64_t(1) << 30))
+        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
+    if (!g.u || !g.delta || !g.B || !g.C || !g.A || !g.dy)
+        return fail(VS_ERR_NULL, "u, delta, B, C, A and dy must not be NULL");
+    if (!g.du || !g.ddelta || !g.dB || !g.dC || !g.dA || !g.dD || !g.dbias)
+        return fail(VS_ERR_NULL, "every gradient output must be given");
+    if (g.z && !g.dz) return fail(VS_ERR_NULL, "dz must not be NULL when z is given");
+    const size_t es = g.dtype == VS_BF16 ? 2 : 4;
+    const void* acts[] = {g.u, g.delta, g.z, g.B, g.C, g.dy, g.du, g.ddelta, g.dz};
+    for (const void* p : acts)
+        if (p && !aligned(p, es)) return fail(VS_ERR_ALIGN, "activation pointer misaligned");
+    const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
+    for (const void* p : fps)
+        if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
+    size_t offs[4];
+    const size_t need = grad_ws_bytes(g.batch, g.dim, g.L, offs);
+    if (!g.ws || g.ws_bytes < need)
+        return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
+    // no output (nor the workspace) may overlap an input or another output
+    const size_t act = static_cast<size_t>(elems) * es;
+    const size_t bc_in = static_cast<size_t>(g.batch * g.dstate * g.L) * es;
+    const size_t bcf = static_cast<size_t>(g.batch * g.dstate * g.L) * 4;
+    const size_t pa = static_cast<size_t>(2 * g.dim * g.dstate) * 4;
+    const size_t pd = static_cast<size_t>(2 * g.dim) * 4;
+    const void* ins[] = {g.u, g.delta, g.z, g.B, g.C, g.A, g.Dskip, g.dt_bias, g.dy};
+    const size_t in_b[] = {act, act, act, bc_in, bc_in, pa, pd, pd, act};
+    const void* outs[] = {g.du, g.ddelta, g.dz, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
+    const size_t out_b[] = {act, act, act, bcf, bcf, pa, pd, pd, need};
+    for (int i = 0; i < 9; ++i) {
+        for (int j = 0; j < 9; ++j)
+            if (overlaps(outs[i], out_b[i], ins[j], in_b[j]))
+                return fail(VS_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
+        for (int j = i + 1; j < 9; ++j)
+            if (overlaps(outs[i], out_b[i], outs[j], out_b[j]))
+                return fail(VS_ERR_ALIAS, "gradient outputs overlap each other or the workspace");
+    }
+    return VS_OK;
+}
+
+template <typename T>
+int launch_grad(const GradCall& g) {
+    size_t offs[4];
+    grad_ws_bytes(g.batch, g.dim, g.L, offs);
+    char* ws = static_cast<char*>(g.ws);
+    float* sbuf = reinterpret_cast<float*>(ws + offs[0]);
+    float* ckpt = reinterpret_cast<float*>(ws + offs[1]);
+    hipStream_t st = static_cast<hipStream_t>(g.stream);
+    const dim3 blk(kThreads);
+    const dim3 grid(static_cast<unsigned>((g.dim + 7) / 8), static_cast<unsigned>(g.batch));
+    const int nblk = static_cast<int>((g.L + kBlockTok - 1) / kBlockTok);
+    // 1. forward pass: merged ungated output (fp32) and the states at every
+    //    block start
+    ScanArgs a{};
+    a.u = g.u; a.delta = g.delta; a.z = nullptr; a.B = g.B; a.C = g.C;
+    a.A = g.A; a.Dskip = g.Dskip; a.dt_bias = g.dt_bias; a.y = nullptr;
+    a.partial = sbuf; a.ckpt = ckpt;
+    a.dim = g.dim; a.L = g.L; a.dstate = static_cast<int>(g.dstate);
+    a.softplus = g.softplus; a.nblk = nblk;
+    if (g.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), grid, blk, 0, st, a);
+    // 2. the summed gradients start from zero
+    float* zs[] = {g.dB, g.dC, g.dA, g.dD, g.dbias};
+    const int64_t zn[] = {g.batch * g.dstate * g.L, g.batch * g.dstate * g.L,
+                          2 * g.dim * g.dstate, 2 * g.dim, 2 * g.dim};
+    for (int i = 0; i < 5; ++i) {
+        const int64_t nb = (zn[i] + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(nb < 4096 ? nb : 4096)), blk,
+                           0, st, zs[i], zn[i]);
+    }
+    // 3. reverse pass
+    GradArgs r{};
+    r.u = g.u; r.delta = g.delta; r.z = g.z; r.B = g.B; r.C = g.C; r.dy = g.dy;
+    r.A = g.A; r.Dskip = g.Dskip; r.dt_bias = g.dt_bias;
+    r.s = sbuf; r.ckpt = ckpt;
+    r.pdu = reinterpret_cast<float*>(ws + offs[2]);
+    r.pdd = reinterpret_cast<float*>(ws + offs[3]);
+    r.du = g.du; r.ddelta = g.ddelta; r.dz = g.dz;
+    r.dB = g.dB; r.dC = g.dC; r.dA = g.dA; r.dD = g.dD; r.dbias = g.dbias;
+    r.dim = g.dim; r.L = g.L; r.dstate = static_cast<int>(g.dstate); r.nblk = nblk;
+    if (g.z && g.softplus)
+        hipLaunchKernelGGL((rowgrad_kernel<T, true, true>), grid, blk, 0, st, r);
+    else if (g.z)
+        hipLaunchKernelGGL((rowgrad_kernel<T, true, false>), grid, blk, 0, st, r);
+    else if (g.softplus)
+        hipLaunchKernelGGL((rowgrad_kernel<T, false, true>), grid, blk, 0, st, r);
+    else
+        hipLaunchKernelGGL((rowgrad_kernel<T, false, false>), grid, blk, 0, st, r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return VS_OK;
+}
+
 int run(const Call& c) {
     g_last_error.clear();
     int rc = validate(c);
@@ -739,6 +1186,10 @@ extern "C" {
 size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype) {
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
     if (dtype != VS_F32 && dtype != VS_BF16) return 0;
+    if (op == VS_OP_VIM_GRAD) {
+        size_t offs[4];
+        return grad_ws_bytes(batch, dim, seqlen, offs);
+    }
     // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
     // cross-scan two; an fp32 y serves as the first. The cross-scan also
     // keeps column-major copies of u and delta (input dtype).
@@ -776,6 +1227,21 @@ int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
     c.conv_w = conv_w;
     c.conv_b = conv_b;
     return run(c);
+}
+
+int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* u, const void* delta, const void* z, const void* B,
+                        const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, const void* dy, void* du, void* ddelta, void* dz,
+                        float* dB, float* dC, float* dA, float* dD, float* ddt_bias,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error.clear();
+    GradCall g{batch, dim, dstate, seqlen, dtype, u, delta, z, B, C, A, Dskip, dt_bias,
+               delta_softplus ? 1 : 0, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
+               workspace, workspace_bytes, stream};
+    const int rc = validate_grad(g);
+    if (rc != VS_OK) return rc;
+    return dtype == VS_BF16 ? launch_grad<uint16_t>(g) : launch_grad<float>(g);
 }
 
 int vmamba_cross_scan4(int64_t batch, int64_t dim, int64_t dstate, int64_t H, int64_t W,

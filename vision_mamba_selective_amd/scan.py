@@ -124,6 +124,43 @@ def vim_scan_bidir_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip=None, dt_bia
     return y
 
 
+def vim_scan_bidir_grad(u, delta, z, B, C, A, Dskip, dt_bias, dy, delta_softplus=True,
+                        workspace=None):
+    """Gradient of vim_scan_bidir for an upstream gradient dy (same shape as
+    y). Returns a dict: du, ddelta, dz (None without z) in the input dtype,
+    [batch, dim, L]; dB, dC fp32 [batch, dstate, L]; dA fp32 [2, dim,
+    dstate]; dD, ddt_bias fp32 [2, dim]."""
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z), ("dy", dy)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+               dz=None if z is None else torch.empty_like(u),
+               dB=torch.empty(batch, dstate, L, **f32), dC=torch.empty(batch, dstate, L, **f32),
+               dA=torch.empty(2, dim, dstate, **f32), dD=torch.empty(2, dim, **f32),
+               ddt_bias=torch.empty(2, dim, **f32))
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_GRAD, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir_grad(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                     _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                     _ptr(dt_bias), int(bool(delta_softplus)), _ptr(dy),
+                                     _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]),
+                                     _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
+                                     _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(ws), ws_bytes,
+                                     _stream(dev))
+    nat.check("vim_scan_bidir_grad", rc)
+    return out
+
+
 def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
                        delta_softplus=True, out=None, workspace=None):
     """VMamba four-direction cross-scan of an H x W grid.
