@@ -80,8 +80,8 @@ enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 }
 #define VS_MAX_DSTATE 16
 
 /* Bytes of device workspace an operation needs (VS_OP_VIM_GRAD: the
- * gradient's forward output, per-block states and partial sums, about
- * 20 bytes per element). Otherwise, in units of E =
+ * gradient's forward output, per-block states, partial sums and the
+ * per-workgroup dB/dC block sums, about 52 bytes per element). Otherwise, in units of E =
  * batch*dim*seqlen elements. Direction merge: fp32 buffers of E floats,
  * one for VS_OP_VIM_BIDIR and two for VS_OP_CROSS4 (one per pair of opposite
  * directions); an fp32 y serves as the first, so fp32 needs one fewer.
@@ -156,9 +156,12 @@ int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
  *                  over batch rows); returned even when Dskip / dt_bias are
  *                  NULL (the gradient at 0)
  *   workspace      at least vs_workspace_bytes(VS_OP_VIM_GRAD, ...) bytes
- * Every output is overwritten. dB, dC, dA, dD and ddt_bias are sums of fp32
- * atomic additions, so their last bits may differ between calls. No output
- * may overlap an input, another output or the workspace (VS_ERR_ALIAS).
+ * Every output is overwritten. du, ddelta, dz, dB and dC are the same bit
+ * for bit on every call (dB and dC are summed in a fixed order); dA, dD and
+ * ddt_bias are sums of fp32 atomic additions, so their last bits may differ
+ * between calls. No output may overlap an input, another output or the
+ * workspace (VS_ERR_ALIAS). Sequences longer than 2^26 tokens return
+ * VS_ERR_UNSUPPORTED.
  */
 int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                         const void* u, const void* delta, const void* z, const void* B,

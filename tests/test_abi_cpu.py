@@ -71,6 +71,10 @@ def fake(i):
     return BASE + i * 256 * MB
 
 
+def far(i):
+    return BASE + i * (8 << 30)    # 8 GiB apart: no overlap at the largest sizes
+
+
 def vim_call(nat, **kw):
     a = dict(batch=2, dim=8, dstate=16, L=33, dtype=nat.VS_BF16, u=fake(0), delta=fake(1),
              z=fake(2), B=fake(3), C=fake(4), A=fake(5), D=fake(6), bias=fake(7), sp=1,
@@ -125,7 +129,6 @@ def test_element_limit(nat):
     """Activation tensors of 2^30 elements or more are refused (the kernels
     address them with 32-bit byte offsets); one element fewer is accepted
     by validation (checked here up to the workspace test only)."""
-    far = lambda i: BASE + i * (8 << 30)    # 8 GiB apart: no overlap at this size
     big = dict(u=far(0), delta=far(1), z=far(2), B=far(3), C=far(4), A=far(5), D=far(6),
                bias=far(7), y=far(8), ws=far(9), ws_bytes=1 << 33)
     assert vim_call(nat, batch=1, dim=16384, L=65536, **big) == -6
@@ -167,6 +170,12 @@ def test_grad_validation(nat):
     assert call(du=fake(0) + 64) == -5           # du inside u
     assert call(dC=fake(10) + 128) == -5         # dC overlaps dB
     assert call(dA=fake(12) + 2) == -4
+    # the gradient caps the sequence at 2^26 tokens (one batch row, one channel)
+    L = (1 << 26) + 1
+    big = nat.lib.vs_workspace_bytes(3, 1, 1, L, nat.VS_F32)
+    assert f(1, 1, 16, L, nat.VS_F32, far(0), far(1), None, far(2), far(3), far(4), None, None,
+             1, far(5), far(6), far(7), None, far(8), far(9), far(10), far(11), far(12), far(13),
+             big, None) == -6
 
 
 def test_1d_validation(nat):

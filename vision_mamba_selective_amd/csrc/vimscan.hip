@@ -569,9 +569,17 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //   * du and ddelta of the two directions merge through fp32 partial sums
 //     as the forward merge does (blocks above F hold first visits, below F
 //     second visits, block F is mixed);
-//   * dB and dC (shared by every channel) are summed over the workgroup's
-//     rows in LDS and added to global memory with fp32 atomics; dA, dD and
-//     dt_bias are summed per row and added once at the end.
+//   * dB and dC are shared by every channel: each lane holds its state's
+//     contributions for the block's 16 steps. A 32-lane swap sums the wave's
+//     two rows of the same direction (dB lands in the low half of the wave,
+//     dC in the high half), LDS sums the four waves, and the workgroup
+//     stores its 1024 block sums (dB|dC x side x state x step) as one
+//     contiguous 4 KB chunk. grad_bc_reduce_kernel then sums the chunks over
+//     the workgroups in a fixed order, so no atomics are involved and dB and
+//     dC repeat bit for bit. dA, dD and dt_bias are summed per row and added
+//     once at the end with atomics.
+constexpr int kBcChunk = 1024;    // floats per workgroup and block: [dB|dC][side][n][step]
+
 struct GradArgs {
     const void *u, *delta, *z, *B, *C, *dy;
     const float *A, *Dskip, *dt_bias;
@@ -579,7 +587,8 @@ struct GradArgs {
     const float* ckpt;      // state at each block start, per row
     float *pdu, *pdd;       // fp32 partial sums of du and ddelta_raw
     void *du, *ddelta, *dz;
-    float *dB, *dC, *dA, *dD, *dbias;
+    float *bc_part;         // [batch][group][block][kBcChunk] dB/dC chunks
+    float *dA, *dD, *dbias;
     int64_t dim, L;
     int dstate, nblk;
 };
@@ -588,11 +597,20 @@ __device__ __forceinline__ float sigmoid_f(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
+// Lanes 0-31 return a[l] + a[l + 32]; lanes 32-63 return b[l - 32] + b[l]
+// (one v_permlane32_swap, which exchanges the upper half of a with the lower
+// half of b, and one add).
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <typename T, bool GATE, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void rowgrad_kernel(const GradArgs a) {
     constexpr int kChPerWg = 8;
     __shared__ __attribute__((aligned(16))) float tile[2][2][2][kRowLanes][kTilePad];
-    __shared__ float gbc[2][2][kRowLanes][kBlockTok];    // [side][dB|dC][n][step]
+    // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap
+    __shared__ __attribute__((aligned(16))) float red[kThreads / kWaveLanes][kWaveLanes][kTilePad];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -666,10 +684,11 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             tile[1][r >> 1][r & 1][sn][slot] = 0.f;
         }
     }
-    // dB/dC accumulators: thread tid owns entries 4 tid .. 4 tid + 3
-    float* const gflat = &gbc[0][0][0][0];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) gflat[4 * tid + e] = 0.f;
+    // after the swap, lane l of a wave holds which = l / 32 (dB, dC),
+    // side = (l / 16) & 1 (the rows' direction) and state l % 16, which is
+    // the chunk's [which][side][n] order
+    float* const bc_chunks = a.bc_part + static_cast<size_t>(b * gridDim.x + cg) * nblk * kBcChunk;
+    float4* const red_lane = reinterpret_cast<float4*>(&red[tid >> 6][lane][0]);
 
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
@@ -677,17 +696,46 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
         return rev ? L - 1 - tc : tc;
     };
     const int Fstep = (L - 1) / (2 * kBlockTok);
-    struct Tok { uint32_t u, dl, z, g; float s; int p; };
+    struct Tok { uint32_t u, dl, z, g; float s, h0; int p; };
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
         k.p = p;
+        const float h0 = ck_row[blk * kRowLanes + n];            // state at the block's start
+        k.h0 = active ? h0 : 0.f;
         k.u = act_at(ub, p);
         k.dl = act_at(db, p);
         k.g = act_at(gb, p);
         if (GATE) {
             k.z = act_at(zb, p);
-            k.s = *f32_at(sb, dir == 0 ? p : 0);   // dz is written by the forward row
+            k.s = *f32_at(sb, p);
         }
+    };
+
+    // Per-token outputs go through buffer descriptors that cover the wave's
+    // two channels; a lane with nothing to store gets the first offset past
+    // that range, which the hardware drops. The loop bodies then have no
+    // divergent branches around memory operations, so the waits the compiler
+    // inserts for the prefetched loads do not also wait for these stores.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);      // uniform per wave
+    const int64_t wave_d0 = static_cast<int64_t>(cg) * kChPerWg + 2 * wave;
+    const int64_t wave_ch = a.dim - wave_d0 < 0 ? 0 : (a.dim - wave_d0 > 2 ? 2 : a.dim - wave_d0);
+    const size_t wave_el = static_cast<size_t>(b * a.dim + (wave_ch > 0 ? wave_d0 : 0)) * a.L;
+    const uint32_t wave_n = static_cast<uint32_t>(wave_ch * a.L);
+    auto rsrc = [&](void* base, uint32_t es) {
+        return __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(base) + wave_el * es, 0,
+                                                 static_cast<int>(wave_n * es), 0x00020000);
+    };
+    const auto r_du = rsrc(a.du, kEs), r_dd = rsrc(a.ddelta, kEs);
+    const auto r_pdu = rsrc(a.pdu, 4), r_pdd = rsrc(a.pdd, 4);
+    const auto r_dz = GATE ? rsrc(a.dz, kEs) : r_du;
+    const uint32_t row_el = static_cast<uint32_t>((d - (wave_ch > 0 ? wave_d0 : 0)) * a.L);
+    auto bst = [&](__amdgpu_buffer_rsrc_t r, uint32_t es, bool on, int p, float v) {
+        const int off = static_cast<int>(on ? (row_el + static_cast<uint32_t>(p)) * es : wave_n * es);
+        if (es == 4)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)),
+                                                  r, off, 0, 0);
     };
 
     uint32_t sr[kStage];
@@ -700,17 +748,21 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
+    // Blocks above F hold every token's first visit (its partial du, ddelta
+    // go to pdu, pdd, and dz is written there), blocks below F the second
+    // (partial added, du and ddelta written); block F mixes both.
+    constexpr int kFirst = 0, kMixed = 1, kSecond = 2;
     float lam = 0.f, e_carry = 0.f, dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
-    auto step = [&](const int blk, Tok& cur, Tok& nxt) {
+    auto step = [&](auto phase, const int blk, Tok& cur, Tok& nxt) {
+        constexpr int PH = decltype(phase)::value;
         const int buf = blk & 1;
         const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
-        // partial sums of the other direction's first visits (blocks below F)
+        // partial sums of the other direction's first visits
         float part_du = 0.f, part_dd = 0.f;
-        {
-            const int pp = blk < Fstep ? p : 0;
-            part_du = __hip_atomic_load(pdu + pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            part_dd = __hip_atomic_load(pdd + pp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (PH == kSecond) {
+            part_du = __hip_atomic_load(pdu + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            part_dd = __hip_atomic_load(pdd + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         const int nb = blk > 0 ? blk - 1 : 0;
         stage_load(nb, sr);
@@ -719,7 +771,8 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
         // this lane's step (slot n) quantities
         const float cu = from_raw<T>(cur.u);
         const float x = from_raw<T>(cur.dl) + bias;
-        const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
+        const float sp = SOFTPLUS ? softplus_f(x) : x;
+        const float dlt = ok ? sp : 0.f;
         const float du_ = dlt * cu;
         const float g = from_raw<T>(cur.g);
         float gs = g;
@@ -727,8 +780,16 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             const float zz = from_raw<T>(cur.z);
             const float sg = sigmoid_f(zz);
             gs = g * zz * sg;
-            if (dir == 0 && ok)
-                st(out_at(a.dz, p), 0, g * cur.s * sg * fmaf(zz, 1.f - sg, 1.f));
+            // dz at the token's first visit
+            const float dzv = g * cur.s * sg * fmaf(zz, 1.f - sg, 1.f);
+            if (PH == kFirst) {
+                bst(r_dz, kEs, ok, p, dzv);
+            } else if (PH == kMixed) {
+                const int t_self = blk * kBlockTok + n;
+                const int blk_other = (L - 1 - t_self) / kBlockTok;
+                if (ok && (blk > blk_other || (blk == blk_other && dir == 0)))
+                    st(out_at(a.dz, p), 0, dzv);
+            }
         }
         gs = ok ? gs : 0.f;
 
@@ -742,7 +803,7 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             Cv[4 * q] = cq.x; Cv[4 * q + 1] = cq.y; Cv[4 * q + 2] = cq.z; Cv[4 * q + 3] = cq.w;
         }
         // recompute the block's states from the stored start state
-        const float h_in = active ? ck_row[blk * kRowLanes + n] : 0.f;
+        const float h_in = cur.h0;
         float hs[16], es[16];
         {
             float h = h_in;
@@ -754,7 +815,7 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             });
         }
         // adjoint, backwards over the block's steps
-        float wv[16], vv[16];
+        float wv[16], vv[16], sbc[16];
         Unroll<16>::run([&](auto ic) {
             constexpr int i = 15 - decltype(ic)::value;
             const float e_next = i < 15 ? es[i < 15 ? i + 1 : 15] : e_carry;
@@ -765,8 +826,7 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             dA_acc = fmaf(q, row_bcast<i>(dlt), dA_acc);
             wv[i] = lam * Bv[i];
             vv[i] = q * An;
-            atomicAdd(&gbc[dir][1][n][i], g_i * hs[i]);
-            atomicAdd(&gbc[dir][0][n][i], lam * row_bcast<i>(du_));
+            sbc[i] = swap32_sum(lam * row_bcast<i>(du_), g_i * hs[i]);
         });
         e_carry = es[0];
         const float Rw = row_transpose_sum(wv, lane);
@@ -779,14 +839,12 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             dD_acc = fmaf(gs, cu, dD_acc);
         }
         // merge the two directions' du and ddelta_raw for this step's token
-        auto finish = [&](float vdu, float vdd) {
-            st(out_at(a.du, p), 0, vdu);
-            st(out_at(a.ddelta, p), 0, vdd);
-        };
-        if (blk > Fstep) {
-            if (ok) { pdu[p] = du_tok; pdd[p] = dx; }
-        } else if (blk < Fstep) {
-            if (ok) finish(du_tok + part_du, dx + part_dd);
+        if (PH == kFirst) {
+            bst(r_pdu, 4, ok, p, du_tok);
+            bst(r_pdd, 4, ok, p, dx);
+        } else if (PH == kSecond) {
+            bst(r_du, kEs, ok, p, du_tok + part_du);
+            bst(r_dd, kEs, ok, p, dx + part_dd);
         } else {
             const int t_self = blk * kBlockTok + n;
             const int blk_other = (L - 1 - t_self) / kBlockTok;
@@ -799,27 +857,28 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
             if (ok && !first) {
                 const float odu = __hip_atomic_load(pdu + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const float odd = __hip_atomic_load(pdd + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                finish(du_tok + odu, dx + odd);
+                st(out_at(a.du, p), 0, du_tok + odu);
+                st(out_at(a.ddelta, p), 0, dx + odd);
             }
         }
 
-        // every row's dB/dC of this block are in gbc: add them to global
-        // memory, clear, and stage the next block's B/C
+        // sum the four waves' dB/dC in LDS into the block's chunk, and
+        // stage the next block's B/C
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            red_lane[q] = make_float4(sbc[4 * q], sbc[4 * q + 1], sbc[4 * q + 2], sbc[4 * q + 3]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        {
+            const int rl = tid >> 2, i0 = (tid & 3) * 4;
+            float4 acc = *reinterpret_cast<const float4*>(&red[0][rl][i0]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int idx = 4 * tid + e;                  // [side][dB|dC][n][i]
-            const int side = idx >> 9, which = (idx >> 8) & 1, sn2 = (idx >> 4) & 15, i = idx & 15;
-            const int t = blk * kBlockTok + i;
-            const float v = gflat[idx];
-            gflat[idx] = 0.f;
-            if (t < L && sn2 < a.dstate) {
-                const int tk = side ? L - 1 - t : t;
-                float* dst = (which ? a.dC : a.dB) + (b * a.dstate + sn2) * a.L + tk;
-                atomicAdd(dst, v);
+            for (int w = 1; w < kThreads / kWaveLanes; ++w) {
+                const float4 v = *reinterpret_cast<const float4*>(&red[w][rl][i0]);
+                acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
+            reinterpret_cast<float4*>(bc_chunks + static_cast<size_t>(blk) * kBcChunk)[tid] = acc;
         }
         stage_store(buf ^ 1, sr);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -827,12 +886,22 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
+    // Each phase is its own loop with the same memory operations on every
+    // trip; everything in flight is drained between the phases.
     int blk = last;
-    for (; blk > 0; blk -= 2) {
-        step(blk, tA, tB);
-        step(blk - 1, tB, tA);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (; blk > Fstep; --blk) {
+        step(std::integral_constant<int, kFirst>{}, blk, tA, tB);
+        tA = tB;
     }
-    if (blk == 0) step(0, tA, tB);
+    __builtin_amdgcn_s_waitcnt(0);
+    step(std::integral_constant<int, kMixed>{}, blk, tA, tB);
+    tA = tB;
+    __builtin_amdgcn_s_waitcnt(0);
+    for (--blk; blk >= 0; --blk) {
+        step(std::integral_constant<int, kSecond>{}, blk, tA, tB);
+        tA = tB;
+    }
 
     // per-row sums: dA (lane n), dD and dt_bias (summed over the row's lanes)
     if (n_ok) atomicAdd(&a.dA[prow * a.dstate + n], dA_acc);
@@ -845,6 +914,35 @@ __global__ __launch_bounds__(kThreads) void rowgrad_kernel(const GradArgs a) {
         atomicAdd(&a.dD[prow], sD);
         atomicAdd(&a.dbias[prow], sb2);
     }
+}
+
+// dB and dC from the gradient kernel's chunks: the sum over the workgroups of
+// side 0 at step t = token t and side 1 at step t = token L-1-t. One thread
+// per (state, token) of a 16-token block; the workgroups are added in a fixed
+// order.
+__global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
+        const float* __restrict__ part, float* __restrict__ dB, float* __restrict__ dC, int64_t L,
+        int dstate, int nblk, int ngroups) {
+    const int n = threadIdx.x >> 4, i = threadIdx.x & 15;
+    const int64_t b = blockIdx.y;
+    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kBlockTok + i;
+    if (n >= dstate || tok >= L) return;
+    const int64_t t1 = L - 1 - tok;
+    // [which][side][n][step]: side 0 for the forward direction, 1 for the backward one
+    const size_t o0 = static_cast<size_t>(blockIdx.x) * kBcChunk + static_cast<size_t>(n) * kBlockTok + i;
+    const size_t o1 = static_cast<size_t>(t1 / kBlockTok) * kBcChunk +
+                      static_cast<size_t>(kRowLanes + n) * kBlockTok + static_cast<size_t>(t1 % kBlockTok);
+    constexpr size_t kC = kBcChunk / 2;
+    const size_t gstride = static_cast<size_t>(nblk) * kBcChunk;
+    const float* c = part + static_cast<size_t>(b) * ngroups * gstride;
+    float sB = 0.f, sC = 0.f;
+    for (int g = 0; g < ngroups; ++g, c += gstride) {
+        sB += c[o0] + c[o1];
+        sC += c[o0 + kC] + c[o1 + kC];
+    }
+    const size_t o = static_cast<size_t>(b * dstate + n) * static_cast<size_t>(L) + static_cast<size_t>(tok);
+    dB[o] = sB;
+    dC[o] = sC;
 }
 
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
@@ -1049,16 +1147,23 @@ struct GradCall {
 
 // workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
 // [du partials: fp32 E][ddelta partials: fp32 E], each 256-byte aligned
-size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[4]) {
+constexpr int kGradChPerWg = 8;
+// the gradient kernel's buffer descriptors span two channels' rows in bytes
+// (2 L x 4 B), which must stay well inside a 32-bit signed range
+constexpr int64_t kGradMaxL = int64_t(1) << 26;
+size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
     const size_t elems = static_cast<size_t>(batch * dim * L);
     const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
     const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
+    const size_t groups = static_cast<size_t>((dim + kGradChPerWg - 1) / kGradChPerWg);
+    const size_t chunks = static_cast<size_t>(batch) * groups * nblk * kBcChunk;
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
-    offs[0] = off; off += al(4 * elems);
-    offs[1] = off; off += al(4 * ck);
-    offs[2] = off; off += al(4 * elems);
-    offs[3] = off; off += al(4 * elems);
+    offs[0] = off; off += al(4 * elems);     // merged ungated forward output
+    offs[1] = off; off += al(4 * ck);        // block-start states
+    offs[2] = off; off += al(4 * elems);     // du partials
+    offs[3] = off; off += al(4 * elems);     // ddelta partials
+    offs[4] = off; off += al(4 * chunks);    // dB/dC chunks
     return off;
 }
 
@@ -1074,6 +1179,7 @@ int validate_grad(const GradCall& g) {
     const int64_t elems = g.batch * g.dim * g.L;
     if (elems >= (int64_t(1) << 30) || g.batch * g.dstate * g.L >= (int64_t(1) << 30))
         return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
+    if (g.L > kGradMaxL) return fail(VS_ERR_UNSUPPORTED, "the gradient supports sequences of up to 2^26 tokens");
     if (!g.u || !g.delta || !g.B || !g.C || !g.A || !g.dy)
         return fail(VS_ERR_NULL, "u, delta, B, C, A and dy must not be NULL");
     if (!g.du || !g.ddelta || !g.dB || !g.dC || !g.dA || !g.dD || !g.dbias)
@@ -1086,7 +1192,7 @@ int validate_grad(const GradCall& g) {
     const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
     for (const void* p : fps)
         if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
-    size_t offs[4];
+    size_t offs[5];
     const size_t need = grad_ws_bytes(g.batch, g.dim, g.L, offs);
     if (!g.ws || g.ws_bytes < need)
         return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
@@ -1113,14 +1219,15 @@ int validate_grad(const GradCall& g) {
 
 template <typename T>
 int launch_grad(const GradCall& g) {
-    size_t offs[4];
+    size_t offs[5];
     grad_ws_bytes(g.batch, g.dim, g.L, offs);
     char* ws = static_cast<char*>(g.ws);
     float* sbuf = reinterpret_cast<float*>(ws + offs[0]);
     float* ckpt = reinterpret_cast<float*>(ws + offs[1]);
     hipStream_t st = static_cast<hipStream_t>(g.stream);
     const dim3 blk(kThreads);
-    const dim3 grid(static_cast<unsigned>((g.dim + 7) / 8), static_cast<unsigned>(g.batch));
+    const unsigned groups = static_cast<unsigned>((g.dim + kGradChPerWg - 1) / kGradChPerWg);
+    const dim3 grid(groups, static_cast<unsigned>(g.batch));
     const int nblk = static_cast<int>((g.L + kBlockTok - 1) / kBlockTok);
     // 1. forward pass: merged ungated output (fp32) and the states at every
     //    block start
@@ -1134,11 +1241,10 @@ int launch_grad(const GradCall& g) {
         hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), grid, blk, 0, st, a);
     else
         hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), grid, blk, 0, st, a);
-    // 2. the summed gradients start from zero
-    float* zs[] = {g.dB, g.dC, g.dA, g.dD, g.dbias};
-    const int64_t zn[] = {g.batch * g.dstate * g.L, g.batch * g.dstate * g.L,
-                          2 * g.dim * g.dstate, 2 * g.dim, 2 * g.dim};
-    for (int i = 0; i < 5; ++i) {
+    // 2. the atomically summed gradients start from zero
+    float* zs[] = {g.dA, g.dD, g.dbias};
+    const int64_t zn[] = {2 * g.dim * g.dstate, 2 * g.dim, 2 * g.dim};
+    for (int i = 0; i < 3; ++i) {
         const int64_t nb = (zn[i] + kThreads - 1) / kThreads;
         hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(nb < 4096 ? nb : 4096)), blk,
                            0, st, zs[i], zn[i]);
@@ -1151,7 +1257,8 @@ int launch_grad(const GradCall& g) {
     r.pdu = reinterpret_cast<float*>(ws + offs[2]);
     r.pdd = reinterpret_cast<float*>(ws + offs[3]);
     r.du = g.du; r.ddelta = g.ddelta; r.dz = g.dz;
-    r.dB = g.dB; r.dC = g.dC; r.dA = g.dA; r.dD = g.dD; r.dbias = g.dbias;
+    r.bc_part = reinterpret_cast<float*>(ws + offs[4]);
+    r.dA = g.dA; r.dD = g.dD; r.dbias = g.dbias;
     r.dim = g.dim; r.L = g.L; r.dstate = static_cast<int>(g.dstate); r.nblk = nblk;
     if (g.z && g.softplus)
         hipLaunchKernelGGL((rowgrad_kernel<T, true, true>), grid, blk, 0, st, r);
@@ -1161,6 +1268,10 @@ int launch_grad(const GradCall& g) {
         hipLaunchKernelGGL((rowgrad_kernel<T, false, true>), grid, blk, 0, st, r);
     else
         hipLaunchKernelGGL((rowgrad_kernel<T, false, false>), grid, blk, 0, st, r);
+    // 4. dB and dC
+    hipLaunchKernelGGL(grad_bc_reduce_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(g.batch)),
+                       blk, 0, st, r.bc_part, g.dB, g.dC, g.L, static_cast<int>(g.dstate), nblk,
+                       static_cast<int>(groups));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return VS_OK;
@@ -1187,7 +1298,7 @@ size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, in
     if (batch < 1 || dim < 1 || seqlen < 1) return 0;
     if (dtype != VS_F32 && dtype != VS_BF16) return 0;
     if (op == VS_OP_VIM_GRAD) {
-        size_t offs[4];
+        size_t offs[5];
         return grad_ws_bytes(batch, dim, seqlen, offs);
     }
     // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
