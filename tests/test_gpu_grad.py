@@ -88,6 +88,29 @@ def test_grad_small(shape, base, gate):
     compare(got, ref, wl.dtype, "grad small")
 
 
+# batch x ceil(dim / 24) >= 256: the launcher takes 24-channel workgroups
+# (768 threads); dims that are not multiples of 24 leave idle channels
+WIDE = [
+    # batch, dim, L, dstate
+    (256, 20, 37, 16),
+    (128, 50, 45, 12),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE)
+@pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
+def test_grad_wide_workgroups(shape, base):
+    b_, d, L, N = shape
+    wl = base.with_(batch=b_, dim=d, seqlen=L, dstate=N, seed=sum(shape) * 19)
+    inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+    dy = upstream(inp, seed=sum(shape) + 1)
+    say("case grad wide%s %s" % (shape, wl.dtype))
+    got = run_grad(inp, dy)
+    ref = oracle.vim_bidir_grad(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D,
+                                inp.dt_bias, dy)
+    compare(got, ref, wl.dtype, "grad wide")
+
+
 @pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
 def test_grad_softplus_off(base):
     wl = base.with_(batch=2, dim=11, seqlen=70)

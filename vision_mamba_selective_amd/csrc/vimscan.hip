@@ -605,12 +605,16 @@ __device__ __forceinline__ float swap32_sum(float a, float b) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, bool GATE, bool SOFTPLUS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void rowgrad_kernel(const GradArgs a) {
-    constexpr int kChPerWg = 8;
+template <typename T, bool GATE, bool SOFTPLUS, int CH>
+__global__ __launch_bounds__(CH * 2 * kRowLanes) __attribute__((amdgpu_waves_per_eu(3)))
+void rowgrad_kernel(const GradArgs a) {
+    // CH channels x {forward, backward} rows per workgroup, two channels per wave
+    constexpr int kChPerWg = CH;
+    constexpr int kWaves = CH / 2;
+    static_assert(CH % 4 == 0, "whole waves, and at least the 256 staging threads");
     __shared__ __attribute__((aligned(16))) float tile[2][2][2][kRowLanes][kTilePad];
     // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap
-    __shared__ __attribute__((aligned(16))) float red[kThreads / kWaveLanes][kWaveLanes][kTilePad];
+    __shared__ __attribute__((aligned(16))) float red[kWaves][kWaveLanes][kTilePad];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -655,9 +659,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* const ck_row =
         a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
 
-    // ---- B/C staging (as rowscan_kernel: side 0 reads token t, side 1 L-1-t)
+    // ---- B/C staging (as rowscan_kernel: side 0 reads token t, side 1 L-1-t),
+    // by the first 256 threads: thread (sn, slot) moves state sn of step slot
     constexpr int kStage = 4;
-    const int sn = tid >> 4, slot = tid & 15;
+    const bool stager = tid < kThreads;
+    const int sn = (tid >> 4) & (kRowLanes - 1), slot = tid & 15;
     const bool sn_ok = sn < a.dstate;
     const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
@@ -673,11 +679,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     };
     const int st_col = sn_ok ? slot : kRowLanes;
     auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) {
+        if (stager) {
 #pragma unroll
-        for (int r = 0; r < kStage; ++r)
-            tile[buf][r >> 1][r & 1][sn][st_col] = from_raw<T>(sr[r]);
+            for (int r = 0; r < kStage; ++r)
+                tile[buf][r >> 1][r & 1][sn][st_col] = from_raw<T>(sr[r]);
+        }
     };
-    if (!sn_ok) {
+    if (stager && !sn_ok) {
 #pragma unroll
         for (int r = 0; r < kStage; ++r) {
             tile[0][r >> 1][r & 1][sn][slot] = 0.f;
@@ -688,6 +696,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // side = (l / 16) & 1 (the rows' direction) and state l % 16, which is
     // the chunk's [which][side][n] order
     float* const bc_chunks = a.bc_part + static_cast<size_t>(b * gridDim.x + cg) * nblk * kBcChunk;
+    // the first 256 threads store the chunk (a float4 each); the others get
+    // an out-of-range offset
+    const int chunk_off = stager ? tid * 16 : kBcChunk * 4;
     float4* const red_lane = reinterpret_cast<float4*>(&red[tid >> 6][lane][0]);
 
     auto tok_pos = [&](int blk) {
@@ -871,14 +882,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         {
-            const int rl = tid >> 2, i0 = (tid & 3) * 4;
+            const int rl = (tid >> 2) & (kWaveLanes - 1), i0 = (tid & 3) * 4;
             float4 acc = *reinterpret_cast<const float4*>(&red[0][rl][i0]);
 #pragma unroll
-            for (int w = 1; w < kThreads / kWaveLanes; ++w) {
+            for (int w = 1; w < kWaves; ++w) {
                 const float4 v = *reinterpret_cast<const float4*>(&red[w][rl][i0]);
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
-            reinterpret_cast<float4*>(bc_chunks + static_cast<size_t>(blk) * kBcChunk)[tid] = acc;
+            const auto rc = __builtin_amdgcn_make_buffer_rsrc(bc_chunks + static_cast<size_t>(blk) * kBcChunk,
+                                                              0, kBcChunk * 4, 0x00020000);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, acc), rc, chunk_off, 0, 0);
         }
         stage_store(buf ^ 1, sr);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -1147,7 +1161,14 @@ struct GradCall {
 
 // workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
 // [du partials: fp32 E][ddelta partials: fp32 E], each 256-byte aligned
-constexpr int kGradChPerWg = 8;
+// Channels per gradient workgroup. With 24 (768 threads, one workgroup per
+// CU at 3 waves per SIMD) the workgroups write a third of the dB/dC chunks
+// that 8 channels (256 threads) write; 24 is used when it still gives every
+// one of the 256 CUs a workgroup.
+constexpr int64_t kNumCUs = 256;
+int grad_channels(int64_t batch, int64_t dim) {
+    return batch * ((dim + 23) / 24) >= kNumCUs ? 24 : 8;
+}
 // the gradient kernel's buffer descriptors span two channels' rows in bytes
 // (2 L x 4 B), which must stay well inside a 32-bit signed range
 constexpr int64_t kGradMaxL = int64_t(1) << 26;
@@ -1155,7 +1176,8 @@ size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
     const size_t elems = static_cast<size_t>(batch * dim * L);
     const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
     const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
-    const size_t groups = static_cast<size_t>((dim + kGradChPerWg - 1) / kGradChPerWg);
+    const int ch = grad_channels(batch, dim);
+    const size_t groups = static_cast<size_t>((dim + ch - 1) / ch);
     const size_t chunks = static_cast<size_t>(batch) * groups * nblk * kBcChunk;
     auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
@@ -1217,6 +1239,19 @@ int validate_grad(const GradCall& g) {
     return VS_OK;
 }
 
+template <typename T, int CH>
+void launch_rowgrad(bool gate, bool softplus, dim3 grid, hipStream_t st, const GradArgs& r) {
+    const dim3 blk(CH * 2 * kRowLanes);
+    if (gate && softplus)
+        hipLaunchKernelGGL((rowgrad_kernel<T, true, true, CH>), grid, blk, 0, st, r);
+    else if (gate)
+        hipLaunchKernelGGL((rowgrad_kernel<T, true, false, CH>), grid, blk, 0, st, r);
+    else if (softplus)
+        hipLaunchKernelGGL((rowgrad_kernel<T, false, true, CH>), grid, blk, 0, st, r);
+    else
+        hipLaunchKernelGGL((rowgrad_kernel<T, false, false, CH>), grid, blk, 0, st, r);
+}
+
 template <typename T>
 int launch_grad(const GradCall& g) {
     size_t offs[5];
@@ -1226,7 +1261,8 @@ int launch_grad(const GradCall& g) {
     float* ckpt = reinterpret_cast<float*>(ws + offs[1]);
     hipStream_t st = static_cast<hipStream_t>(g.stream);
     const dim3 blk(kThreads);
-    const unsigned groups = static_cast<unsigned>((g.dim + kGradChPerWg - 1) / kGradChPerWg);
+    const int ch = grad_channels(g.batch, g.dim);
+    const unsigned groups = static_cast<unsigned>((g.dim + ch - 1) / ch);
     const dim3 grid(groups, static_cast<unsigned>(g.batch));
     const int nblk = static_cast<int>((g.L + kBlockTok - 1) / kBlockTok);
     // 1. forward pass: merged ungated output (fp32) and the states at every
@@ -1237,10 +1273,12 @@ int launch_grad(const GradCall& g) {
     a.partial = sbuf; a.ckpt = ckpt;
     a.dim = g.dim; a.L = g.L; a.dstate = static_cast<int>(g.dstate);
     a.softplus = g.softplus; a.nblk = nblk;
+    constexpr int kFwdCh = 8;      // rowscan_kernel (Vim): 8 channels x 2 directions per workgroup
+    const dim3 fgrid(static_cast<unsigned>((g.dim + kFwdCh - 1) / kFwdCh), static_cast<unsigned>(g.batch));
     if (g.softplus)
-        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), fgrid, blk, 0, st, a);
     else
-        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), grid, blk, 0, st, a);
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), fgrid, blk, 0, st, a);
     // 2. the atomically summed gradients start from zero
     float* zs[] = {g.dA, g.dD, g.dbias};
     const int64_t zn[] = {2 * g.dim * g.dstate, 2 * g.dim, 2 * g.dim};
@@ -1260,14 +1298,10 @@ int launch_grad(const GradCall& g) {
     r.bc_part = reinterpret_cast<float*>(ws + offs[4]);
     r.dA = g.dA; r.dD = g.dD; r.dbias = g.dbias;
     r.dim = g.dim; r.L = g.L; r.dstate = static_cast<int>(g.dstate); r.nblk = nblk;
-    if (g.z && g.softplus)
-        hipLaunchKernelGGL((rowgrad_kernel<T, true, true>), grid, blk, 0, st, r);
-    else if (g.z)
-        hipLaunchKernelGGL((rowgrad_kernel<T, true, false>), grid, blk, 0, st, r);
-    else if (g.softplus)
-        hipLaunchKernelGGL((rowgrad_kernel<T, false, true>), grid, blk, 0, st, r);
+    if (ch == 24)
+        launch_rowgrad<T, 24>(g.z != nullptr, g.softplus != 0, grid, st, r);
     else
-        hipLaunchKernelGGL((rowgrad_kernel<T, false, false>), grid, blk, 0, st, r);
+        launch_rowgrad<T, 8>(g.z != nullptr, g.softplus != 0, grid, st, r);
     // 4. dB and dC
     hipLaunchKernelGGL(grad_bc_reduce_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(g.batch)),
                        blk, 0, st, r.bc_part, g.dB, g.dC, g.L, static_cast<int>(g.dstate), nblk,
