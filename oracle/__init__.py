@@ -81,22 +81,24 @@ def _ptr(a):
 
 def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
          bc_per_direction: bool, H: int = 0, W: int = 0, delta_softplus: bool = True,
-         nthreads: Optional[int] = None, lib=None, u_per_direction: bool = False) -> np.ndarray:
+         nthreads: Optional[int] = None, lib=None, u_per_direction: bool = False,
+         delta_per_direction: bool = False) -> np.ndarray:
     """Generic scan: len(orders) directions, merged by sum, optional gate.
 
-    u, delta, z: [batch, dim, L] (u: [ndir, batch, dim, L] when
-    u_per_direction); B, C: [batch, dstate, L] (shared, token order) or
+    u, delta, z: [batch, dim, L] (u, delta: [ndir, batch, dim, L] when
+    u_per_direction, delta_per_direction); B, C: [batch, dstate, L] (shared, token order) or
     [batch, ndir, dstate, L] (per direction, scan order);
     A: [ndir, dim, dstate]; Dskip, dt_bias: [ndir, dim] or None.
     """
     lib = lib or load()
     u, delta, z, B, C, A = map(_f64, (u, delta, z, B, C, A))
     Dskip, dt_bias = _f64(Dskip), _f64(dt_bias)
-    batch, dim, L = delta.shape
+    batch, dim, L = delta.shape[-3:]
     ndir = len(orders)
     assert u.shape == ((ndir,) if u_per_direction else ()) + (batch, dim, L)
+    assert delta.shape == ((ndir,) if delta_per_direction else ()) + (batch, dim, L)
     dstate = A.shape[-1]
-    assert z is None or z.shape == delta.shape
+    assert z is None or z.shape == (batch, dim, L)
     assert A.shape == (ndir, dim, dstate)
     if bc_per_direction:
         assert B.shape == (batch, ndir, dstate, L) and C.shape == B.shape
@@ -107,13 +109,30 @@ def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
     order = np.ascontiguousarray(orders, dtype=np.intc)
     y = np.empty((batch, dim, L), np.float64)
     rc = lib.oracle_scan_ex_f64(batch, dim, dstate, L, H, W, ndir, _ptr(order), _ptr(u),
-                                int(bool(u_per_direction)), _ptr(delta), _ptr(z), _ptr(B),
+                                int(bool(u_per_direction)) | (2 if delta_per_direction else 0),
+                                _ptr(delta), _ptr(z), _ptr(B),
                                 _ptr(C), int(bc_per_direction), _ptr(A), _ptr(Dskip),
                                 _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y),
                                 nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_scan_ex_f64 failed with status %d" % rc)
     return y
+
+
+def vim_dirs(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None):
+    """Vim with per-direction inputs (the guide's block code gives each branch
+    its own conv and SimpleSelectiveSSM, hence its own u, delta, B, C):
+    u, delta [2, batch, dim, L] and B, C [batch, 2, dstate, L], all in token
+    order; z [batch, dim, L] (shared gate) or None. The backward direction
+    visits token L-1-t at step t, so its B, C are passed to the scan in that
+    order (a flip)."""
+    B, C = _f64(B), _f64(C)
+    Bs, Cs = B.copy(), C.copy()
+    Bs[:, 1] = B[:, 1, :, ::-1]
+    Cs[:, 1] = C[:, 1, :, ::-1]
+    return scan(u, delta, z, Bs, Cs, A, Dskip, dt_bias, orders=(ORD_FORWARD, ORD_REVERSE),
+                bc_per_direction=True, delta_softplus=delta_softplus, nthreads=nthreads,
+                u_per_direction=True, delta_per_direction=True)
 
 
 def vim_bidir(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None):

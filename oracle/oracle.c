@@ -68,6 +68,9 @@ static double softplus(double x)
     return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
 }
 
+#define PER_DIR_U 1
+#define PER_DIR_DELTA 2
+
 typedef struct {
     int batch, dim, dstate;
     long L, H, W;
@@ -76,8 +79,9 @@ typedef struct {
     const double *u, *delta, *z, *B, *C, *A, *Dskip, *dt_bias;
     int bc_per_direction;   /* 0: B, C are [batch][dstate][L] in token order;
                                1: [batch][ndir][dstate][L] in scan order */
-    int u_per_direction;    /* 0: u is [batch][dim][L], shared by the directions;
-                               1: [ndir][batch][dim][L], one per direction */
+    int per_direction;      /* bit 0 (PER_DIR_U): u is [ndir][batch][dim][L], one per
+                               direction, else [batch][dim][L], shared; bit 1
+                               (PER_DIR_DELTA): the same for delta_raw */
     int delta_softplus;
     double* y;
     /* work split */
@@ -90,14 +94,16 @@ static void run_unit(const job_t* J, long unit, double* h, double* acc)
 {
     const long b = unit / J->dim, d = unit % J->dim;
     const long L = J->L, N = J->dstate;
-    const double* dl = J->delta + (b * J->dim + d) * L;
+    const long copy = (long)J->batch * J->dim * L;       /* elements of one direction's copy */
     double* y = J->y + (b * J->dim + d) * L;
 
     for (long p = 0; p < L; ++p) acc[p] = 0.0;
 
     for (int k = 0; k < J->ndir; ++k) {
-        const double* u = J->u + (J->u_per_direction ? (long)k * J->batch * J->dim * L : 0)
+        const double* u = J->u + ((J->per_direction & PER_DIR_U) ? k * copy : 0)
                           + (b * J->dim + d) * L;
+        const double* dl = J->delta + ((J->per_direction & PER_DIR_DELTA) ? k * copy : 0)
+                           + (b * J->dim + d) * L;
         const double* A = J->A + ((long)k * J->dim + d) * N;
         const double Dk = J->Dskip ? J->Dskip[(long)k * J->dim + d] : 0.0;
         const double bias = J->dt_bias ? J->dt_bias[(long)k * J->dim + d] : 0.0;
@@ -149,11 +155,13 @@ static void* worker(void* arg)
     return NULL;
 }
 
-/* Generic entry: ndir directions with the given visiting orders; u shared
- * (u_per_direction = 0) or one per direction (1).
+/* Generic entry: ndir directions with the given visiting orders; u and
+ * delta_raw each shared or one per direction (per_direction bits PER_DIR_U,
+ * PER_DIR_DELTA). The guide's Vim block code gives each branch its own conv
+ * and its own SimpleSelectiveSSM projections, hence its own u, delta, B, C.
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure. */
 int oracle_scan_ex_f64(int batch, int dim, int dstate, long L, long H, long W,
-                       int ndir, const int* order, const double* u, int u_per_direction,
+                       int ndir, const int* order, const double* u, int per_direction,
                        const double* delta, const double* z, const double* B, const double* C,
                        int bc_per_direction, const double* A, const double* Dskip,
                        const double* dt_bias, int delta_softplus, double* y, int nthreads)
@@ -179,7 +187,7 @@ int oracle_scan_ex_f64(int batch, int dim, int dstate, long L, long H, long W,
         J->u = u; J->delta = delta; J->z = z; J->B = B; J->C = C;
         J->A = A; J->Dskip = Dskip; J->dt_bias = dt_bias;
         J->bc_per_direction = bc_per_direction; J->delta_softplus = delta_softplus;
-        J->u_per_direction = u_per_direction ? 1 : 0;
+        J->per_direction = per_direction & (PER_DIR_U | PER_DIR_DELTA);
         J->y = y;
         J->unit_begin = units * i / nthreads;
         J->unit_end = units * (i + 1) / nthreads;

@@ -138,7 +138,7 @@ def test_grad_per_token_outputs_are_repeatable():
         assert torch.equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("idx", [1, 2])
+@pytest.mark.parametrize("idx", [1, 2, 5])
 def test_grad_workload_full_size(idx):
     """The Vim-S workloads at full size against the full oracle gradient
     (every channel contributes to dB and dC)."""

@@ -131,7 +131,7 @@ def sample_rows(wl, nch=24):
     return batches, ch
 
 
-@pytest.mark.parametrize("idx", [0, 1, 2, 4])
+@pytest.mark.parametrize("idx", [0, 1, 2, 4, 5])
 def test_vim_workload_full_size(idx):
     wl = wlm.WORKLOADS[idx]
     say("case workload %d %s" % (idx, wl.name))

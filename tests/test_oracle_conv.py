@@ -125,8 +125,7 @@ CONV_MUTATIONS = {
                                   "u[(rows + r) * L + t] = silu(c[t]);"),
     "sigmoid_not_silu": ("static double silu(double v) { return v / (1.0 + exp(-v)); }",
                          "static double silu(double v) { return 1.0 / (1.0 + exp(-v)); }"),
-    "u_shared_not_per_direction": ("(J->u_per_direction ? (long)k * J->batch * J->dim * L : 0)",
-                                   "0"),
+    "u_shared_not_per_direction": ("((J->per_direction & PER_DIR_U) ? k * copy : 0)", "0"),
     "backward_uses_forward_taps": ("conv_w + ((long)dim + d) * 3", "conv_w + d * 3"),
 }
 

@@ -74,3 +74,9 @@ def test_channel_subset_matches_slices():
     assert np.array_equal(sub.u, inp.u[:, [3, 7]])
     assert np.array_equal(sub.A, inp.A[:, [3, 7]])
     assert sub.wl.dim == 2
+
+
+def test_high_resolution_workload_shape():
+    """1248 x 1248 pixels at 16 x 16 patches plus the class token."""
+    wl = wlm.WORKLOADS[5]
+    assert (wl.kind, wl.seqlen, wl.dim, wl.dstate, wl.dtype) == ("vim", 6085, 768, 16, wlm.BF16)

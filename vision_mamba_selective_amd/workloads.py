@@ -12,6 +12,10 @@ trained weights exist here):
   and 2048x2048 images at 16x16 patches give 196, 4,096 and 16,384 patches;
   section "1. Patch Tokenization and Position Embedding" prepends one class
   token, so a Vim sequence has 197, 4,097 or 16,385 tokens.
+* Same page, section "Empirical Benchmarks & Performance Analysis", table
+  "Classification & High-Resolution Benchmark Comparison": Vim-S at 1248x1248
+  (78 x 78 patches of 16 pixels plus the class token: 6,085 tokens). The page
+  gives no batch size; batch 8 matches the 1024x1024 workload.
 * Same page, section "VMamba: 2D Selective Scan (SS2D) and Cross-Scan
   Traversal": a feature grid unrolled in four orders (64x64 here).
 * Same page, section "PyTorch Implementation of the Bidirectional Vision Mamba
@@ -98,7 +102,8 @@ def _vim(name, batch, seqlen, dim, dtype, dt_min, dt_max, seed):
                     seed=seed)
 
 
-#: The five workloads. Index 2 (Vim-S at 1024^2) is the throughput headline.
+#: The workloads. Index 2 (Vim-S at 1024^2) is the throughput headline; index
+#: 5 (Vim-S at 1248^2) is the resolution of the guide's memory comparison.
 WORKLOADS = [
     _vim("vim_ti_224_f32", 1, 197, 384, F32, 1e-3, 1e-1, 1000),
     _vim("vim_s_224_bf16", 64, 197, 768, BF16, 1e-3, 1e-1, 1001),
@@ -107,6 +112,7 @@ WORKLOADS = [
              dstate=16, seqlen=64 * 64, dtype=F32, dt_min=1e-3, dt_max=1e-1,
              H=64, W=64, gate=False, seed=1003),
     _vim("vim_b_2048_bf16", 2, 16385, 1536, BF16, 1e-4, 1e-1, 1004),
+    _vim("vim_s_1248_bf16", 8, (1248 // 16) ** 2 + 1, 768, BF16, 1e-3, 1e-1, 1005),
 ]
 
 HEADLINE = 2
