@@ -113,6 +113,26 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    void* stream);
 
 /*
+ * vim_scan_bidir with per-direction inputs. In the guide's block code
+ * (section "1. PyTorch Implementation of the Bidirectional Vision Mamba
+ * Block") each branch has its own conv1d and its own SimpleSelectiveSSM,
+ * whose projections give that branch its own u, delta, B and C.
+ *   u, delta       [2][batch][dim][L]: copy 0 feeds the forward direction,
+ *                  copy 1 the backward one; token order in both
+ *   B, C           [batch][2][dstate][L]: direction k's rows, token order
+ *                  (the backward direction reads token L-1-t at step t)
+ *   z              [batch][dim][L] or NULL: one gate on the merged output
+ *   everything else as for vim_scan_bidir (same workspace). A caller that
+ *   holds the backward branch in its own (flipped) order flips it first.
+ * Returns VS_ERR_UNSUPPORTED when 2*batch*dim*L reaches 2^30.
+ */
+int vim_scan_bidir_dirs(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* u, const void* delta, const void* z, const void* B,
+                        const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * vim_scan_bidir with the Vim block's front end fused into the token loads:
  * each branch's scan input is u_k = silu(conv_k(x)), a depthwise Conv1d with
  * kernel 3, padding 1 and bias, applied to x in the forward branch and to

@@ -111,6 +111,27 @@ def test_vim_validation(nat, kw, code):
     assert nat.lib.vs_last_error() != b""
 
 
+def test_dirs_validation(nat):
+    """vim_scan_bidir_dirs: u and delta hold two copies, B and C two
+    direction blocks, so both the size limit and the overlap checks see
+    twice the bytes of vim_scan_bidir."""
+    f = nat.lib.vim_scan_bidir_dirs
+
+    def call(batch=2, dim=8, L=33, u=fake(0), delta=fake(1), B=fake(3), y=fake(8), ptr=fake):
+        return f(batch, dim, 16, L, nat.VS_BF16, u, delta, None, B, ptr(4), ptr(5), None, None, 1,
+                 y, ptr(9), 1 << 20, None)
+    act = 2 * 8 * 33 * 2                            # bytes of one bf16 copy
+    # (every call here fails validation, so no kernel is ever launched)
+    assert call(y=fake(0) + act + 64) == -5         # y inside u's second copy
+    # the same y is outside vim_scan_bidir's u: that call gets as far as the
+    # workspace check
+    assert vim_call(nat, y=fake(0) + act + 64, ws=None) == -8
+    bc = 2 * 16 * 33 * 2                            # bytes of one direction's B block
+    assert call(y=fake(3) + bc + 64) == -5          # y inside B's backward block
+    L = 1 << 29                                     # 2 * batch * dim * L reaches 2^30
+    assert call(batch=1, dim=1, L=L, u=far(0), delta=far(1), B=far(3), y=far(8), ptr=far) == -6
+
+
 def test_cross4_validation(nat):
     f = nat.lib.vmamba_cross_scan4
     args = [fake(0), fake(1), None, fake(3), fake(4), fake(5), None, None, 1, fake(8), fake(9),

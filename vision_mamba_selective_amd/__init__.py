@@ -7,9 +7,8 @@ The binding is imported lazily so that the generator can be used without the
 library.
 """
 
-__all__ = ["vim_scan_bidir", "vim_scan_bidir_conv", "vim_scan_bidir_grad", "vmamba_cross_scan4",
-           "s6_scan_1d",
-           "workspace_bytes"]
+__all__ = ["vim_scan_bidir", "vim_scan_bidir_dirs", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
+           "vmamba_cross_scan4", "s6_scan_1d", "workspace_bytes"]
 
 
 def __getattr__(name):

@@ -25,6 +25,8 @@ SIGNATURES = {
     "vs_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "vim_scan_bidir": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                             _P, _P, _SZ, _P]),
+    "vim_scan_bidir_dirs": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                 _P, _P, _SZ, _P]),
     "vim_scan_bidir_conv": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _I, _P, _P, _SZ, _P]),
     "vim_scan_bidir_grad": (_I, [_I64, _I64, _I64, _I64, _I] + [_P] * 8 + [_I] + [_P] * 9 +

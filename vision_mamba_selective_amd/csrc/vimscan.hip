@@ -66,6 +66,12 @@ struct ScanArgs {
     float* ckpt;            // gradient recompute: state at each block start
     const float* conv_w;    // Vim front end: depthwise taps [2][dim][3] (u holds x)
     const float* conv_b;    // and biases [2][dim] (NULL: 0)
+    // Vim with per-direction inputs: the backward rows read u and delta this
+    // many elements past the forward rows' (0: shared), and B, C are
+    // [batch][2][dstate][L] in token order when bc_per_dir is set
+    uint32_t u_dir_off;
+    uint32_t dl_dir_off;
+    int bc_per_dir;
     int64_t dim;
     int64_t L;
     int H;
@@ -307,6 +313,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto act_at = [&](const char* base, int p) {
         return ld_raw(reinterpret_cast<const T*>(base + (rowoff + static_cast<uint32_t>(p)) * kEs), 0);
     };
+    const uint32_t u_row = rowoff + (MODE == kModeVim && rev ? a.u_dir_off : 0u);
+    const uint32_t dl_row = rowoff + (MODE == kModeVim && rev ? a.dl_dir_off : 0u);
+    auto act_row = [&](const char* base, uint32_t row, int p) {
+        return ld_raw(reinterpret_cast<const T*>(base + (row + static_cast<uint32_t>(p)) * kEs), 0);
+    };
     auto part_at = [&](int p) {
         return reinterpret_cast<float*>(pb + (rowoff + static_cast<uint32_t>(p)) * 4u);
     };
@@ -322,9 +333,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     constexpr int kStage = kSides * 2;
     const int sn = tid >> 4, slot = tid & 15;
     const bool sn_ok = sn < a.dstate;
-    const int64_t bc_dirs = MODE == kModeCross4 ? 4 : 1;
+    const int64_t bc_dirs = MODE == kModeCross4 ? 4 : (MODE == kModeVim && a.bc_per_dir ? 2 : 1);
     const uint32_t bc_row = static_cast<uint32_t>((b * bc_dirs * a.dstate + (sn_ok ? sn : 0)) * a.L);
     const uint32_t bc_dir_stride = static_cast<uint32_t>(a.dstate * a.L);
+    const uint32_t vim_side_stride = MODE == kModeVim && a.bc_per_dir ? bc_dir_stride : 0u;
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
     const char* __restrict__ Cb = static_cast<const char*>(a.C);
     auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
@@ -338,7 +350,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
                        static_cast<uint32_t>(tc)) * kEs;
             } else {
                 const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
-                off = (bc_row + static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
+                off = (bc_row + (side_rev ? vim_side_stride : 0u) +
+                       static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
             }
             sr[r] = ld_raw(reinterpret_cast<const T*>(((r & 1) ? Cb : Bb) + off), 0);
         }
@@ -374,12 +387,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
         k.p = p;
-        k.u = act_at(ub, p);
+        k.u = act_row(ub, u_row, p);
         if (CONV) {   // the neighbours (clamped; masked where they fall outside)
-            k.ul = act_at(ub, p > 0 ? p - 1 : 0);
-            k.ur = act_at(ub, p < L - 1 ? p + 1 : L - 1);
+            k.ul = act_row(ub, u_row, p > 0 ? p - 1 : 0);
+            k.ur = act_row(ub, u_row, p < L - 1 ? p + 1 : L - 1);
         }
-        k.dl = act_at(db, p);
+        k.dl = act_row(db, dl_row, p);
         // z is needed only by the visit that finishes the token; other
         // blocks load entry 0 of the row (one cached line) instead of
         // branching, which would stall on the in-flight registers. The
@@ -1027,6 +1040,7 @@ struct Call {
     void* stream;
     const float* conv_w = nullptr;   // Vim front end (u then holds x)
     const float* conv_b = nullptr;
+    bool per_dir = false;            // Vim: u, delta [2][batch][dim][L]; B, C [batch][2][N][L]
 };
 
 int64_t ndirs(int mode) { return mode == kModeVim ? 2 : (mode == kModeCross4 ? 4 : 1); }
@@ -1045,6 +1059,9 @@ int validate(const Call& c) {
     // sums included), so each tensor must stay below 4 GiB
     if (elems >= (int64_t(1) << 30) || c.batch * 4 * c.dstate * c.L >= (int64_t(1) << 30))
         return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
+    const int64_t copies = c.per_dir ? 2 : 1;     // direction copies of u, delta, B and C
+    if (copies * elems >= (int64_t(1) << 30))
+        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
     if (!c.u || !c.delta || !c.B || !c.C || !c.A || !c.y)
         return fail(VS_ERR_NULL, "u, delta, B, C, A and y must not be NULL");
     const size_t es = c.dtype == VS_BF16 ? 2 : 4;
@@ -1056,12 +1073,13 @@ int validate(const Call& c) {
         if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
     const int64_t nd = ndirs(c.mode);
     const size_t act = static_cast<size_t>(elems) * es;
-    const size_t bc = static_cast<size_t>(c.batch * (c.mode == kModeCross4 ? 4 : 1) * c.dstate *
-                                          c.L) * es;
+    const size_t bc = static_cast<size_t>(c.batch * (c.mode == kModeCross4 ? 4 : copies) *
+                                          c.dstate * c.L) * es;
+    const size_t act_in = act * static_cast<size_t>(copies);
     const size_t a_bytes = static_cast<size_t>(nd * c.dim * c.dstate) * 4;
     const size_t p_bytes = static_cast<size_t>(nd * c.dim) * 4;
     const void* ins[] = {c.u, c.delta, c.z, c.B, c.C, c.A, c.Dskip, c.dt_bias, c.conv_w, c.conv_b};
-    const size_t in_bytes[] = {act, act, act, bc, bc, a_bytes, p_bytes, p_bytes, 3 * p_bytes,
+    const size_t in_bytes[] = {act_in, act_in, act, bc, bc, a_bytes, p_bytes, p_bytes, 3 * p_bytes,
                                p_bytes};
     constexpr int kIns = 10;
     for (int i = 0; i < kIns; ++i)
@@ -1089,6 +1107,8 @@ int launch_t(const Call& c) {
     a.u = c.u; a.delta = c.delta; a.z = c.z; a.B = c.B; a.C = c.C;
     a.A = c.A; a.Dskip = c.Dskip; a.dt_bias = c.dt_bias; a.y = c.y;
     a.conv_w = c.conv_w; a.conv_b = c.conv_b;
+    a.u_dir_off = a.dl_dir_off = c.per_dir ? static_cast<uint32_t>(c.batch * c.dim * c.L) : 0u;
+    a.bc_per_dir = c.per_dir ? 1 : 0;
     // merge buffers: fp32 y doubles as the first one; the cross-scan's second
     // pair always uses the workspace (after the first buffer if y is bf16)
     float* ws = static_cast<float*>(c.ws);
@@ -1357,6 +1377,16 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
     return run(c);
 }
 
+int vim_scan_bidir_dirs(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                        const void* u, const void* delta, const void* z, const void* B,
+                        const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                        int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
+           A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    c.per_dir = true;
+    return run(c);
+}
 int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                         const void* x, const float* conv_w, const float* conv_b,
                         const void* delta, const void* z, const void* B, const void* C,

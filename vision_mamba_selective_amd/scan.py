@@ -88,6 +88,36 @@ def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplu
     return y
 
 
+def vim_scan_bidir_dirs(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
+                        out=None, workspace=None):
+    """vim_scan_bidir with per-direction inputs: u, delta [2, batch, dim, L]
+    and B, C [batch, 2, dstate, L], token order (copy 0 forward, copy 1
+    backward); z [batch, dim, L] or None. Returns y [batch, dim, L]."""
+    _, batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    _act("u", u, (2, batch, dim, L), dt, dev)
+    _act("delta", delta, (2, batch, dim, L), dt, dev)
+    if z is not None:
+        _act("z", z, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, 2, dstate, L), dt, dev)
+    _act("C", C, (batch, 2, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    y = torch.empty(batch, dim, L, dtype=dt, device=dev) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir_dirs(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                     _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                     _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _ptr(ws),
+                                     ws_bytes, _stream(dev))
+    nat.check("vim_scan_bidir_dirs", rc)
+    return y
+
+
 def vim_scan_bidir_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip=None, dt_bias=None,
                         delta_softplus=True, out=None, workspace=None):
     """vim_scan_bidir with the Vim block's conv front end fused in: each
