@@ -82,7 +82,7 @@ def _ptr(a):
 def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
          bc_per_direction: bool, H: int = 0, W: int = 0, delta_softplus: bool = True,
          nthreads: Optional[int] = None, lib=None, u_per_direction: bool = False,
-         delta_per_direction: bool = False) -> np.ndarray:
+         delta_per_direction: bool = False, zoh: bool = False) -> np.ndarray:
     """Generic scan: len(orders) directions, merged by sum, optional gate.
 
     u, delta, z: [batch, dim, L] (u, delta: [ndir, batch, dim, L] when
@@ -112,14 +112,15 @@ def scan(u, delta, z, B, C, A, Dskip, dt_bias, *, orders: Sequence[int],
                                 int(bool(u_per_direction)) | (2 if delta_per_direction else 0),
                                 _ptr(delta), _ptr(z), _ptr(B),
                                 _ptr(C), int(bc_per_direction), _ptr(A), _ptr(Dskip),
-                                _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y),
-                                nthreads or default_threads())
+                                _ptr(dt_bias), int(bool(delta_softplus)) | (2 if zoh else 0),
+                                _ptr(y), nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_scan_ex_f64 failed with status %d" % rc)
     return y
 
 
-def vim_dirs(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None):
+def vim_dirs(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None,
+             zoh=False):
     """Vim with per-direction inputs (the guide's block code gives each branch
     its own conv and SimpleSelectiveSSM, hence its own u, delta, B, C):
     u, delta [2, batch, dim, L] and B, C [batch, 2, dstate, L], all in token
@@ -132,17 +133,19 @@ def vim_dirs(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads
     Cs[:, 1] = C[:, 1, :, ::-1]
     return scan(u, delta, z, Bs, Cs, A, Dskip, dt_bias, orders=(ORD_FORWARD, ORD_REVERSE),
                 bc_per_direction=True, delta_softplus=delta_softplus, nthreads=nthreads,
-                u_per_direction=True, delta_per_direction=True)
+                u_per_direction=True, delta_per_direction=True, zoh=zoh)
 
 
-def vim_bidir(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None):
+def vim_bidir(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True, nthreads=None,
+              zoh=False):
     """Vim: forward + backward over shared u, delta, z, B, C."""
     return scan(u, delta, z, B, C, A, Dskip, dt_bias, orders=(ORD_FORWARD, ORD_REVERSE),
-                bc_per_direction=False, delta_softplus=delta_softplus, nthreads=nthreads)
+                bc_per_direction=False, delta_softplus=delta_softplus, nthreads=nthreads,
+                zoh=zoh)
 
 
 def vim_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True,
-             nthreads=None, lib=None):
+             nthreads=None, lib=None, zoh=False):
     """Vim with its conv front end: u_f = silu(conv_f(x)), u_b the flipped
     branch's silu(conv_b(flip x)). x: [batch, dim, L]; conv_w: [2, dim, 3];
     conv_b: [2, dim] or None; the rest as for vim_bidir."""
@@ -157,7 +160,8 @@ def vim_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip, dt_bias, delta_softplu
     y = np.empty((batch, dim, L), np.float64)
     rc = lib.oracle_vim_conv_f64(batch, dim, dstate, L, _ptr(x), _ptr(conv_w), _ptr(conv_b),
                                  _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                                 _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y),
+                                 _ptr(dt_bias), int(bool(delta_softplus)) | (2 if zoh else 0),
+                                 _ptr(y),
                                  nthreads or default_threads())
     if rc != 0:
         raise ValueError("oracle_vim_conv_f64 failed with status %d" % rc)
@@ -193,30 +197,31 @@ def vim_bidir_grad(u, delta, z, B, C, A, Dskip, dt_bias, g, delta_softplus=True,
     return out
 
 
-def cross4(u, delta, z, B, C, A, Dskip, dt_bias, H, W, delta_softplus=True, nthreads=None):
+def cross4(u, delta, z, B, C, A, Dskip, dt_bias, H, W, delta_softplus=True, nthreads=None,
+           zoh=False):
     """VMamba cross-scan: row-major, reversed, column-major, reversed."""
     return scan(u, delta, z, B, C, A, Dskip, dt_bias,
                 orders=(ORD_FORWARD, ORD_REVERSE, ORD_COLUMN, ORD_COLUMN_REVERSE),
-                bc_per_direction=True, H=H, W=W, delta_softplus=delta_softplus,
+                bc_per_direction=True, H=H, W=W, delta_softplus=delta_softplus, zoh=zoh,
                 nthreads=nthreads)
 
 
 def s6_1d(u, delta, z, B, C, A, Dskip, dt_bias, reverse=False, delta_softplus=True,
-          nthreads=None):
+          nthreads=None, zoh=False):
     """A single direction. A: [dim, dstate]; Dskip, dt_bias: [dim] or None."""
     A = np.asarray(A)[None]
     Dskip = None if Dskip is None else np.asarray(Dskip)[None]
     dt_bias = None if dt_bias is None else np.asarray(dt_bias)[None]
     return scan(u, delta, z, B, C, A, Dskip, dt_bias,
                 orders=(ORD_REVERSE if reverse else ORD_FORWARD,), bc_per_direction=False,
-                delta_softplus=delta_softplus, nthreads=nthreads)
+                delta_softplus=delta_softplus, nthreads=nthreads, zoh=zoh)
 
 
-def run_inputs(inp, nthreads=None) -> np.ndarray:
+def run_inputs(inp, nthreads=None, zoh=False) -> np.ndarray:
     """The oracle on a ``workloads.Inputs`` bundle (the workload decides the kind)."""
     wl = inp.wl
     if wl.kind == "vim":
         return vim_bidir(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias,
-                         nthreads=nthreads)
+                         nthreads=nthreads, zoh=zoh)
     return cross4(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias,
-                  wl.H, wl.W, nthreads=nthreads)
+                  wl.H, wl.W, nthreads=nthreads, zoh=zoh)

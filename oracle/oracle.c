@@ -14,8 +14,9 @@
  *
  *  - Continuous-Time State Space Equations: y = C h + D x, D a scalar skip.
  *  - Discretization via Zero-Order Hold: A_bar = exp(delta A); B_bar is
- *    approximated by delta B (the form the page's code uses); recurrence
- *    h_t = A_bar h_{t-1} + B_bar x_t, read-out y_t = C h_t.
+ *    approximated by delta B (the form the page's code uses), or, on
+ *    request, the exact hold (exp(delta A) - 1) / A B the same section states
+ *    first; recurrence h_t = A_bar h_{t-1} + B_bar x_t, read-out y_t = C h_t.
  *  - The Selective State Space (S6) Mechanism box: delta_t = softplus(...),
  *    B_t, C_t input dependent, so A_bar and B_bar change with t.
  *  - PyTorch code, SimpleSelectiveSSM.forward: h starts at zero, A is
@@ -30,7 +31,9 @@
  * Readings where the pages leave a step open (each one is listed with its
  * reason in the design notes):
  *  - D is applied per direction (y_k += D_k u); D = 0 disables it.
- *  - delta_raw + dt_bias goes through softplus when delta_softplus != 0.
+ *  - delta_raw + dt_bias goes through softplus when bit 0 of the flags
+ *    word (the delta_softplus argument) is set; bit 1 selects the exact
+ *    zero-order-hold B_bar.
  *  - Vim directions share u, delta_raw, z, B and C (spatial order); VMamba
  *    directions share u, delta_raw (spatial order) and have their own B and C,
  *    stored in each direction's scan order.
@@ -83,6 +86,7 @@ typedef struct {
                                direction, else [batch][dim][L], shared; bit 1
                                (PER_DIR_DELTA): the same for delta_raw */
     int delta_softplus;
+    int zoh;                /* B_bar = (exp(delta A) - 1) / A B, else delta B */
     double* y;
     /* work split */
     long unit_begin, unit_end;
@@ -125,7 +129,9 @@ static void run_unit(const job_t* J, long unit, double* h, double* acc)
             double yk = 0.0;
             for (long n = 0; n < N; ++n) {
                 const double Abar = exp(delta * A[n]);              /* exp(delta A) */
-                const double Bbar_x = delta * Bk[n * L + q] * u[p]; /* delta B x */
+                double Bbar_x = delta * Bk[n * L + q] * u[p];       /* delta B x */
+                if (J->zoh)   /* exact hold: (exp(delta A) - 1) / A B x; delta B x at A = 0 */
+                    Bbar_x = (A[n] != 0.0 ? expm1(A[n] * delta) / A[n] : delta) * Bk[n * L + q] * u[p];
                 h[n] = Abar * h[n] + Bbar_x;
                 yk += Ck[n * L + q] * h[n];                         /* C_t h_t */
             }
@@ -186,7 +192,9 @@ int oracle_scan_ex_f64(int batch, int dim, int dstate, long L, long H, long W,
         J->L = L; J->H = H; J->W = W; J->ndir = ndir; J->order = order;
         J->u = u; J->delta = delta; J->z = z; J->B = B; J->C = C;
         J->A = A; J->Dskip = Dskip; J->dt_bias = dt_bias;
-        J->bc_per_direction = bc_per_direction; J->delta_softplus = delta_softplus;
+        J->bc_per_direction = bc_per_direction;
+        J->delta_softplus = delta_softplus & 1;
+        J->zoh = (delta_softplus & 2) != 0;
         J->per_direction = per_direction & (PER_DIR_U | PER_DIR_DELTA);
         J->y = y;
         J->unit_begin = units * i / nthreads;
