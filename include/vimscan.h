@@ -76,6 +76,15 @@ enum {
 /* operation kinds for vs_workspace_bytes */
 enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 };
 
+/* The delta_softplus argument of the scan entry points is a flags word.
+ * VS_FLAG_SOFTPLUS: delta = softplus(delta_raw + dt_bias), else delta_raw +
+ * dt_bias. VS_FLAG_ZOH: B_bar = (exp(delta A) - 1) / A * B, the exact
+ * zero-order hold of "Discretization via Zero-Order Hold (ZOH)" (delta B
+ * at A = 0), instead of the delta * B the guide's code uses. Other bits
+ * return VS_ERR_UNSUPPORTED; the gradient takes VS_FLAG_SOFTPLUS only. */
+#define VS_FLAG_SOFTPLUS 1
+#define VS_FLAG_ZOH 2
+
 /* Largest supported state size (the pages use 16 by default and 8 in a test). */
 #define VS_MAX_DSTATE 16
 
@@ -100,7 +109,8 @@ size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, in
  *   B, C           [batch][dstate][L], shared by both directions (token order)
  *   A              [2][dim][dstate] fp32, direction 0 = forward, 1 = backward
  *   Dskip, dt_bias [2][dim] fp32, or NULL for zeros
- *   delta_softplus 1: delta = softplus(delta_raw + dt_bias); 0: no softplus
+ *   delta_softplus flags: VS_FLAG_SOFTPLUS (delta = softplus(delta_raw +
+ *                  dt_bias), else no softplus) | VS_FLAG_ZOH (exact hold)
  *   y              [batch][dim][L], written completely
  *   workspace      at least vs_workspace_bytes(VS_OP_VIM_BIDIR, ...) bytes
  *                  (may be NULL when that is 0); contents on entry are

@@ -132,6 +132,18 @@ def test_dirs_validation(nat):
     assert call(batch=1, dim=1, L=L, u=far(0), delta=far(1), B=far(3), y=far(8), ptr=far) == -6
 
 
+def test_flag_validation(nat):
+    """Bits other than VS_FLAG_SOFTPLUS | VS_FLAG_ZOH are refused, and the
+    gradient takes VS_FLAG_SOFTPLUS only (both before any launch)."""
+    assert vim_call(nat, sp=4) == -6
+    assert vim_call(nat, sp=3, ws=None) == -8          # both known flags get past the check
+    f = nat.lib.vim_scan_bidir_grad
+    need = nat.lib.vs_workspace_bytes(3, 2, 8, 33, nat.VS_BF16)
+    assert f(2, 8, 16, 33, nat.VS_BF16, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+             None, None, 3, fake(6), fake(7), fake(8), fake(9), fake(10), fake(11), fake(12),
+             fake(13), fake(14), fake(15), need, None) == -6
+
+
 def test_cross4_validation(nat):
     f = nat.lib.vmamba_cross_scan4
     args = [fake(0), fake(1), None, fake(3), fake(4), fake(5), None, None, 1, fake(8), fake(9),

@@ -1,0 +1,122 @@
+"""GPU parity of the exact zero-order-hold variant (VS_FLAG_ZOH: B_bar =
+(exp(delta A) - 1) / A B) against the fp64 oracle, element by element,
+through the C ABI, for every forward entry point. Random A (-U(0.1, 20))
+with delta from 1e-3 up puts |delta A| on both sides of the kernel's switch
+between the series for (e^x - 1) / x and the held difference; one state
+has A = 0 exactly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close, dev, host64, run_gpu, say, torch_dtype, upload
+from vision_mamba_selective_amd import workloads as wlm
+
+pytestmark = pytest.mark.gpu
+
+VIM_F32 = wlm.WORKLOADS[0]
+VIM_BF16 = wlm.WORKLOADS[1]
+X4_F32 = wlm.WORKLOADS[3]
+
+SMALL = [
+    # batch, dim, L, dstate
+    (1, 3, 2, 16),
+    (2, 13, 37, 16),
+    (1, 8, 197, 16),
+    (3, 10, 64, 8),
+    (1, 7, 255, 12),
+]
+
+
+def zoh_inputs(wl):
+    inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+    inp.A[..., 1] = 0.0            # the hold's limit: delta * B
+    return inp
+
+
+@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
+def test_zoh_vim_small(shape, base):
+    b_, d, L, N = shape
+    wl = base.with_(batch=b_, dim=d, seqlen=L, dstate=N, seed=sum(shape) * 29)
+    inp = zoh_inputs(wl)
+    say("case zoh vim small%s %s" % (shape, wl.dtype))
+    t = upload(inp)
+    import vision_mamba_selective_amd as vms
+    y = host64(vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"],
+                                  t["Dskip"], t["dt_bias"], zoh=True))
+    ref = oracle.run_inputs(inp, zoh=True)
+    err = assert_close(y, ref, wl.dtype, "zoh vim")
+    say("  max rel err %.3g" % err)
+    if L >= 37:   # the variant is not the delta B form
+        assert not np.allclose(ref, oracle.run_inputs(inp), rtol=1e-3, atol=1e-3)
+
+
+@pytest.mark.parametrize("base", [X4_F32, X4_F32.with_(dtype=wlm.BF16)], ids=["f32", "bf16"])
+def test_zoh_cross4_small(base):
+    wl = base.with_(batch=2, dim=5, H=7, W=9, seqlen=63, gate=True, seed=77)
+    inp = zoh_inputs(wl)
+    say("case zoh cross4 %s" % wl.dtype)
+    import vision_mamba_selective_amd as vms
+    t = upload(inp)
+    y = host64(vms.vmamba_cross_scan4(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], 7, 9,
+                                      t["Dskip"], t["dt_bias"], zoh=True))
+    assert_close(y, oracle.run_inputs(inp, zoh=True), wl.dtype, "zoh cross4")
+
+
+@pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
+def test_zoh_conv_and_dirs(base):
+    import vision_mamba_selective_amd as vms
+    wl = base.with_(batch=2, dim=9, seqlen=70, seed=78)
+    inp = zoh_inputs(wl)
+    dt = torch_dtype(wl)
+    t = upload(inp)
+    rng = np.random.default_rng(79)
+    w = (0.6 * rng.standard_normal((2, 9, 3))).astype(np.float32)
+    cb = (0.2 * rng.standard_normal((2, 9))).astype(np.float32)
+    say("case zoh conv %s" % wl.dtype)
+    y = host64(vms.vim_scan_bidir_conv(t["u"], dev(w, torch.float32), dev(cb, torch.float32),
+                                       t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
+                                       t["dt_bias"], zoh=True))
+    ref = oracle.vim_conv(inp.u, w, cb, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D,
+                          inp.dt_bias, zoh=True)
+    assert_close(y, ref, wl.dtype, "zoh conv")
+    say("case zoh dirs %s" % wl.dtype)
+    other = wlm.make_inputs(wl, seed=wl.seed + 1)
+    u2, d2 = np.stack([inp.u, other.u]), np.stack([inp.delta, other.delta])
+    B2, C2 = np.stack([inp.B, other.B], 1), np.stack([inp.C, other.C], 1)
+    y = host64(vms.vim_scan_bidir_dirs(dev(u2, dt), dev(d2, dt), t["z"], dev(B2, dt), dev(C2, dt),
+                                       t["A"], t["Dskip"], t["dt_bias"], zoh=True))
+    ref = oracle.vim_dirs(u2, d2, inp.z, B2, C2, inp.A, inp.D, inp.dt_bias, zoh=True)
+    assert_close(y, ref, wl.dtype, "zoh dirs")
+
+
+def test_zoh_1d_both_directions():
+    import vision_mamba_selective_amd as vms
+    wl = VIM_F32.with_(batch=2, dim=6, seqlen=45, seed=80)
+    inp = zoh_inputs(wl)
+    t = upload(inp)
+    for rev in (False, True):
+        say("case zoh 1d reverse=%s" % rev)
+        y = host64(vms.s6_scan_1d(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"][0],
+                                  t["Dskip"][0], t["dt_bias"][0], reverse=rev, zoh=True))
+        ref = oracle.s6_1d(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A[0], inp.D[0],
+                           inp.dt_bias[0], reverse=rev, zoh=True)
+        assert_close(y, ref, wl.dtype, "zoh 1d")
+
+
+def test_zoh_workload_full_size():
+    """Vim-S 1024x1024 with the exact hold, sampled (batch, channel) rows."""
+    import vision_mamba_selective_amd as vms
+    wl = wlm.WORKLOADS[2]
+    inp = wlm.make_inputs(wl)
+    t = upload(inp)
+    say("case zoh workload %s" % wl.name)
+    y = vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
+                           t["dt_bias"], zoh=True)
+    batches = [0, wl.batch - 1]
+    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, 16).astype(int), [7, 8]]))
+    sub = wlm.channel_subset(inp, batches, ch)
+    got = host64(y[batches][:, ch.tolist()])
+    err = assert_close(got, oracle.run_inputs(sub, zoh=True), wl.dtype, "zoh full size")
+    say("  sampled max rel err %.3g" % err)

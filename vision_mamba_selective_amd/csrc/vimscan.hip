@@ -159,6 +159,7 @@ __device__ __forceinline__ float row_transpose_sum(const float (&c)[16], int lan
 
 // ---------------------------------------------------------------- math
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // softplus(x) = max(x, 0) + log1p(w), w = e^{-|x|} in (0, 1].
 // log1p(w) = 2 atanh(r) with r = w / (2 + w) in (0, 1/3], summed as the odd
@@ -242,13 +243,17 @@ struct Unroll<0> {
 // sums are read only after it. Vim finishes a token by gating and storing
 // y; the cross-scan stores the pair's sum, and after the loop the workgroup
 // adds its two pairs' sums, gates and stores y.
-template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false>
+template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false,
+          bool ZOH = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
     // CKPT (the gradient's forward pass): store every row's state at each
     // block start and, in place of y, the merged ungated sum in the partial
     // buffer (fp32)
     static_assert(!CKPT || (MODE == kModeVim && !GATE), "checkpoints: ungated Vim only");
+    // ZOH: the exact zero-order hold B_bar = (exp(delta A) - 1) / A B ("Discretization
+    // via Zero-Order Hold (ZOH)") in place of delta B
+    static_assert(!(ZOH && CKPT), "the gradient uses delta B");
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
@@ -284,7 +289,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 
     // per-row parameters
     const int64_t prow = (MODE == kMode1D ? 0 : dir * a.dim) + d;
-    const float A2 = (active && n < a.dstate) ? a.A[prow * a.dstate + n] * kLog2e : 0.f;
+    const float An = (active && n < a.dstate) ? a.A[prow * a.dstate + n] : 0.f;
+    const float A2 = An * kLog2e;
+    const float rA = ZOH ? 1.f / An : 0.f;    // A = 0 only ever takes the series below
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
     // Vim front end: each branch's u = silu(b + w0 x[q-1] + w1 x[q] + w2 x[q+1])
@@ -461,8 +468,24 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         float c[16];
         Unroll<16>::run([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            const float e = __builtin_amdgcn_exp2f(row_bcast<i>(dlt) * A2);
-            h = fmaf(e, h, row_bcast<i>(du) * Bv[i]);
+            const float xl = row_bcast<i>(dlt) * A2;            // delta A log2(e)
+            const float e = __builtin_amdgcn_exp2f(xl);
+            float bu = row_bcast<i>(du);                        // B_bar u / B = delta u
+            if (ZOH) {
+                // (e - 1) / A u when |delta A| >= 1/2; below that the
+                // subtraction cancels, so delta u phi(delta A) with
+                // phi(x) = (e^x - 1) / x = sum x^k / (k + 1)!, to x^6
+                const float xn = xl * kLn2;
+                float phi = fmaf(xn, 1.f / 5040.f, 1.f / 720.f);
+                phi = fmaf(xn, phi, 1.f / 120.f);
+                phi = fmaf(xn, phi, 1.f / 24.f);
+                phi = fmaf(xn, phi, 1.f / 6.f);
+                phi = fmaf(xn, phi, 0.5f);
+                phi = fmaf(xn, phi, 1.f);
+                const float held = (e - 1.f) * rA * row_bcast<i>(cu);
+                bu = fabsf(xn) < 0.5f ? bu * phi : held;
+            }
+            h = fmaf(e, h, bu * Bv[i]);
             c[i] = Cv[i] * h;
         });
         const float yk = fmaf(Dk, cu, row_transpose_sum(c, lane));
@@ -1041,6 +1064,7 @@ struct Call {
     const float* conv_w = nullptr;   // Vim front end (u then holds x)
     const float* conv_b = nullptr;
     bool per_dir = false;            // Vim: u, delta [2][batch][dim][L]; B, C [batch][2][N][L]
+    bool zoh = false;                // exact zero-order-hold B_bar
 };
 
 int64_t ndirs(int mode) { return mode == kModeVim ? 2 : (mode == kModeCross4 ? 4 : 1); }
@@ -1101,6 +1125,18 @@ int validate(const Call& c) {
     return VS_OK;
 }
 
+template <typename T, int MODE, bool CONV, bool ZOH>
+void launch_scan(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a) {
+    if (c.z && c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, true, CONV, false, ZOH>), grid, blk, 0, st, a);
+    else if (c.z)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, false, CONV, false, ZOH>), grid, blk, 0, st, a);
+    else if (c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, true, CONV, false, ZOH>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, false, CONV, false, ZOH>), grid, blk, 0, st, a);
+}
+
 template <typename T, int MODE>
 int launch_t(const Call& c) {
     ScanArgs a;
@@ -1142,23 +1178,20 @@ int launch_t(const Call& c) {
                            const_cast<T*>(static_cast<const T*>(a.uT)),
                            const_cast<T*>(static_cast<const T*>(a.deltaT)), c.H, c.W, rows);
     }
-    if (MODE == kModeVim && c.conv_w) {
-        if (c.z && c.softplus)
-            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, true, true>), grid, blk, 0, st, a);
-        else if (c.z)
-            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, false, true>), grid, blk, 0, st, a);
-        else if (c.softplus)
-            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, true>), grid, blk, 0, st, a);
-        else
-            hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, true>), grid, blk, 0, st, a);
-    } else if (c.z && c.softplus)
-        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, true>), grid, blk, 0, st, a);
-    else if (c.z)
-        hipLaunchKernelGGL((rowscan_kernel<T, MODE, true, false>), grid, blk, 0, st, a);
-    else if (c.softplus)
-        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, true>), grid, blk, 0, st, a);
-    else
-        hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, false>), grid, blk, 0, st, a);
+    if constexpr (MODE == kModeVim) {
+        if (c.conv_w) {
+            if (c.zoh) launch_scan<T, MODE, true, true>(c, grid, blk, st, a);
+            else launch_scan<T, MODE, true, false>(c, grid, blk, st, a);
+        } else if (c.zoh) {
+            launch_scan<T, MODE, false, true>(c, grid, blk, st, a);
+        } else {
+            launch_scan<T, MODE, false, false>(c, grid, blk, st, a);
+        }
+    } else if (c.zoh) {
+        launch_scan<T, MODE, false, true>(c, grid, blk, st, a);
+    } else {
+        launch_scan<T, MODE, false, false>(c, grid, blk, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return VS_OK;
@@ -1211,6 +1244,8 @@ size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
 
 int validate_grad(const GradCall& g) {
     if (g.dtype != VS_F32 && g.dtype != VS_BF16) return fail(VS_ERR_DTYPE, "unknown dtype");
+    if (g.softplus & ~VS_FLAG_SOFTPLUS)
+        return fail(VS_ERR_UNSUPPORTED, "the gradient takes VS_FLAG_SOFTPLUS only (delta B form)");
     if (g.batch < 1 || g.dim < 1 || g.L < 1 || g.dstate < 1)
         return fail(VS_ERR_SHAPE, "batch, dim, dstate and the sequence length must be >= 1");
     if (g.dstate > VS_MAX_DSTATE)
@@ -1331,8 +1366,13 @@ int launch_grad(const GradCall& g) {
     return VS_OK;
 }
 
-int run(const Call& c) {
+int run(Call c) {
     g_last_error.clear();
+    // the delta_softplus argument is a flags word: VS_FLAG_SOFTPLUS, VS_FLAG_ZOH
+    if (c.softplus & ~(VS_FLAG_SOFTPLUS | VS_FLAG_ZOH))
+        return fail(VS_ERR_UNSUPPORTED, "unknown flag bits");
+    c.zoh = (c.softplus & VS_FLAG_ZOH) != 0;
+    c.softplus &= VS_FLAG_SOFTPLUS;
     int rc = validate(c);
     if (rc != VS_OK) return rc;
     const bool bf = c.dtype == VS_BF16;
@@ -1412,7 +1452,7 @@ int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error.clear();
     GradCall g{batch, dim, dstate, seqlen, dtype, u, delta, z, B, C, A, Dskip, dt_bias,
-               delta_softplus ? 1 : 0, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
+               delta_softplus, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
                workspace, workspace_bytes, stream};
     const int rc = validate_grad(g);
     if (rc != VS_OK) return rc;

@@ -18,6 +18,12 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else t.data_ptr()
 
 
+def _flags(delta_softplus, zoh):
+    """The flags word of the scan entry points: VS_FLAG_SOFTPLUS (1) and
+    VS_FLAG_ZOH (2, the exact zero-order hold B_bar = (exp(delta A) - 1)/A B)."""
+    return (1 if delta_softplus else 0) | (2 if zoh else 0)
+
+
 def _act(name, t, shape, dtype, device):
     if t.dtype != dtype:
         raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
@@ -57,7 +63,7 @@ def _workspace(op, batch, dim, seqlen, dtype, device, workspace):
 
 
 def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
-                   out=None, workspace=None):
+                   zoh=False, out=None, workspace=None):
     """Vim forward + backward selective scan, merged and gated.
 
     u, delta, z: [batch, dim, L] (fp32 or bf16; z may be None);
@@ -82,14 +88,14 @@ def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplu
     ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
     rc = nat.lib.vim_scan_bidir(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta), _ptr(z),
                                 _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip), _ptr(dt_bias),
-                                int(bool(delta_softplus)), _ptr(y), _ptr(ws), ws_bytes,
+                                _flags(delta_softplus, zoh), _ptr(y), _ptr(ws), ws_bytes,
                                 _stream(dev))
     nat.check("vim_scan_bidir", rc)
     return y
 
 
 def vim_scan_bidir_dirs(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
-                        out=None, workspace=None):
+                        zoh=False, out=None, workspace=None):
     """vim_scan_bidir with per-direction inputs: u, delta [2, batch, dim, L]
     and B, C [batch, 2, dstate, L], token order (copy 0 forward, copy 1
     backward); z [batch, dim, L] or None. Returns y [batch, dim, L]."""
@@ -112,14 +118,14 @@ def vim_scan_bidir_dirs(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_so
     ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
     rc = nat.lib.vim_scan_bidir_dirs(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
                                      _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                                     _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _ptr(ws),
+                                     _ptr(dt_bias), _flags(delta_softplus, zoh), _ptr(y), _ptr(ws),
                                      ws_bytes, _stream(dev))
     nat.check("vim_scan_bidir_dirs", rc)
     return y
 
 
 def vim_scan_bidir_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip=None, dt_bias=None,
-                        delta_softplus=True, out=None, workspace=None):
+                        delta_softplus=True, zoh=False, out=None, workspace=None):
     """vim_scan_bidir with the Vim block's conv front end fused in: each
     branch scans u_k = silu(conv_k(x)) (depthwise kernel 3, padding 1; the
     backward branch on the flipped sequence).
@@ -148,7 +154,7 @@ def vim_scan_bidir_conv(x, conv_w, conv_b, delta, z, B, C, A, Dskip=None, dt_bia
     rc = nat.lib.vim_scan_bidir_conv(batch, dim, dstate, L, _DTYPES[dt], _ptr(x), _ptr(conv_w),
                                      _ptr(conv_b), _ptr(delta), _ptr(z), _ptr(B), _ptr(C),
                                      _ptr(A), _ptr(Dskip), _ptr(dt_bias),
-                                     int(bool(delta_softplus)), _ptr(y), _ptr(ws), ws_bytes,
+                                     _flags(delta_softplus, zoh), _ptr(y), _ptr(ws), ws_bytes,
                                      _stream(dev))
     nat.check("vim_scan_bidir_conv", rc)
     return y
@@ -192,7 +198,7 @@ def vim_scan_bidir_grad(u, delta, z, B, C, A, Dskip, dt_bias, dy, delta_softplus
 
 
 def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
-                       delta_softplus=True, out=None, workspace=None):
+                       delta_softplus=True, zoh=False, out=None, workspace=None):
     """VMamba four-direction cross-scan of an H x W grid.
 
     u, delta, z: [batch, dim, H*W] (row-major grid; z may be None);
@@ -219,14 +225,14 @@ def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
     ws, ws_bytes = _workspace(nat.VS_OP_CROSS4, batch, dim, L, dt, dev, workspace)
     rc = nat.lib.vmamba_cross_scan4(batch, dim, dstate, H, W, _DTYPES[dt], _ptr(u), _ptr(delta),
                                     _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                                    _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _ptr(ws),
+                                    _ptr(dt_bias), _flags(delta_softplus, zoh), _ptr(y), _ptr(ws),
                                     ws_bytes, _stream(dev))
     nat.check("vmamba_cross_scan4", rc)
     return y
 
 
 def s6_scan_1d(u, delta, z, B, C, A, Dskip=None, dt_bias=None, reverse=False,
-               delta_softplus=True, out=None):
+               delta_softplus=True, zoh=False, out=None):
     """One direction of the scan. A: [dim, dstate]; Dskip, dt_bias: [dim]."""
     batch, dim, L = u.shape
     dstate = A.shape[-1]
@@ -245,6 +251,6 @@ def s6_scan_1d(u, delta, z, B, C, A, Dskip=None, dt_bias=None, reverse=False,
     _act("out", y, (batch, dim, L), dt, dev)
     rc = nat.lib.s6_scan_1d(batch, dim, dstate, L, _DTYPES[dt], int(bool(reverse)), _ptr(u),
                             _ptr(delta), _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
-                            _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _stream(dev))
+                            _ptr(dt_bias), _flags(delta_softplus, zoh), _ptr(y), _stream(dev))
     nat.check("s6_scan_1d", rc)
     return y
