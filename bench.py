@@ -57,6 +57,12 @@ def parse():
     p.add_argument("--grad", action="store_true",
                    help="time vim_scan_bidir_grad: the reverse-mode gradient of the scan for a "
                         "synthetic upstream gradient (forward recompute + adjoint pass)")
+    p.add_argument("--zoh", action="store_true",
+                   help="exact zero-order-hold B_bar = (exp(delta A) - 1) / A B (VS_FLAG_ZOH) "
+                        "instead of delta B")
+    p.add_argument("--dirs", action="store_true",
+                   help="time vim_scan_bidir_dirs: per-direction u, delta, B and C (a second "
+                        "seeded draw feeds the backward direction)")
     p.add_argument("--copy-probe", action="store_true",
                    help="instead of the scan, run torch copies of known size (counter scale)")
     return p.parse_args()
@@ -92,11 +98,14 @@ def main():
 
     idx = wlm.HEADLINE if args.workload is None else args.workload
     wl = wlm.WORKLOADS[idx]
-    if (args.conv or args.grad) and wl.kind != "vim":
-        print("--conv and --grad apply to the Vim workloads only", file=sys.stderr)
+    if (args.conv or args.grad or args.dirs) and wl.kind != "vim":
+        print("--conv, --grad and --dirs apply to the Vim workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.conv and args.grad:
-        print("--conv and --grad are separate measurements", file=sys.stderr)
+    if args.conv + args.grad + args.dirs > 1:
+        print("--conv, --grad and --dirs are separate measurements", file=sys.stderr)
+        sys.exit(2)
+    if args.zoh and args.grad:
+        print("the gradient uses the delta B form; --zoh is a forward option", file=sys.stderr)
         sys.exit(2)
     tdt = torch.bfloat16 if wl.dtype == wlm.BF16 else torch.float32
     print("bench: workload %s" % wl.name, file=sys.stderr, flush=True)
@@ -116,6 +125,13 @@ def main():
         grng = np.random.default_rng(wl.seed + 600)
         gy = grng.standard_normal(inp.u.shape).astype(np.float32)
         base["dy"] = up(wlm.round_bf16(gy) if wl.dtype == wlm.BF16 else gy, tdt)
+    if args.dirs:
+        # the backward direction's copies from a second draw of the recipe
+        other = wlm.make_inputs(wl, seed=wl.seed + 1)
+        base["u"] = torch.stack([base["u"], up(other.u, tdt)]).contiguous()
+        base["delta"] = torch.stack([base["delta"], up(other.delta, tdt)]).contiguous()
+        base["B"] = torch.stack([base["B"], up(other.B, tdt)], 1).contiguous()
+        base["C"] = torch.stack([base["C"], up(other.C, tdt)], 1).contiguous()
     if args.conv:
         crng = np.random.default_rng(wl.seed + 500)
         base["cw"] = up((0.6 * crng.standard_normal((2, wl.dim, 3))).astype(np.float32),
@@ -124,7 +140,7 @@ def main():
                         torch.float32)
     for s in range(nsets):
         t = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
-        t["y"] = torch.empty_like(t["u"])
+        t["y"] = torch.empty(wl.batch, wl.dim, wl.seqlen, dtype=tdt, device=dev)
         t["ws"] = None
         op = 3 if args.grad else (0 if wl.kind == "vim" else 1)
         need = vms.workspace_bytes(op, wl.batch, wl.dim, wl.seqlen, tdt)
@@ -159,13 +175,17 @@ def main():
             grad_call(t)
         elif args.conv:
             vms.vim_scan_bidir_conv(t["u"], t["cw"], t["cb"], t["delta"], t["z"], t["B"], t["C"],
-                                    t["A"], t["D"], t["bias"], out=t["y"], workspace=t["ws"])
+                                    t["A"], t["D"], t["bias"], out=t["y"], workspace=t["ws"],
+                                    zoh=args.zoh)
+        elif args.dirs:
+            vms.vim_scan_bidir_dirs(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
+                                    t["bias"], out=t["y"], workspace=t["ws"], zoh=args.zoh)
         elif wl.kind == "vim":
             vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
-                               t["bias"], out=t["y"], workspace=t["ws"])
+                               t["bias"], out=t["y"], workspace=t["ws"], zoh=args.zoh)
         else:
             vms.vmamba_cross_scan4(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], wl.H, wl.W,
-                                   t["D"], t["bias"], out=t["y"], workspace=t["ws"])
+                                   t["D"], t["bias"], out=t["y"], workspace=t["ws"], zoh=args.zoh)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -191,6 +211,8 @@ def main():
     tc = wl.tokens_channels
     value = tc / (ms_per_step * 1e-3) / 1e9
     alg_bytes = wl.algorithmic_bytes()
+    if args.dirs:   # the second copies of u, delta, B and C
+        alg_bytes += 2 * tc * wl.act_bytes + 2 * wl.batch * wl.dstate * wl.seqlen * wl.act_bytes
     hbm_gbs = alg_bytes / kern_avg_s / 1e9
     updates = wl.state_updates
     upd_rate = updates / kern_avg_s
@@ -200,7 +222,8 @@ def main():
         try:
             with open(PROFILE_TRAFFIC) as f:
                 tr = json.load(f)
-            rec = tr.get(wl.name + ("+conv" if args.conv else "") + ("+grad" if args.grad else ""))
+            rec = tr.get(wl.name + ("+conv" if args.conv else "") + ("+grad" if args.grad else "")
+                         + ("+dirs" if args.dirs else "") + ("+zoh" if args.zoh else ""))
             if rec and rec.get("kernel_sha") == kernel_hash():
                 traffic = rec.get("bytes_per_launch")
         except (OSError, ValueError):
@@ -223,7 +246,9 @@ def main():
                    "d_state": wl.dstate, "seq_len": wl.seqlen, "directions": wl.ndir,
                    "state_dtype": "f32", "input_sets_rotated": nsets,
                    "front_end": "conv1d k3 + silu, fused" if args.conv else "none",
-                   "pass": "gradient (forward recompute + adjoint)" if args.grad else "forward"},
+                   "pass": "gradient (forward recompute + adjoint)" if args.grad else "forward",
+                   "discretization": "exact zero-order hold" if args.zoh else "delta B",
+                   "inputs": "per-direction u, delta, B, C" if args.dirs else "shared"},
         "hbm_GBps": round(hbm_gbs, 1),
         "kernel_ms": round(kern_avg_s * 1e3, 5),
         "roofline": {
@@ -248,11 +273,12 @@ def main():
         if args.conv:
             conv = (base["cw"].cpu().numpy(), base["cb"].cpu().numpy())
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv,
-                                           base["dy"].float().cpu().numpy() if args.grad else None)
+                                           base["dy"].float().cpu().numpy() if args.grad else None,
+                                           zoh=args.zoh, dirs=args.dirs)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, nch, conv=None, dy=None):
+def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False):
     """The fp64 oracle, as it stands, on the host cores of this machine."""
     import numpy as np
     import oracle
@@ -273,13 +299,21 @@ def cpu_baseline(wl, inp, nch, conv=None, dy=None):
         oracle.vim_bidir_grad(sample.u, sample.delta, sample.z, sample.B, sample.C, sample.A,
                               sample.D, sample.dt_bias, np.ascontiguousarray(gy),
                               nthreads=threads)
+    elif dirs:
+        other = wlm.make_inputs(wl, seed=wl.seed + 1)
+        if nch:
+            other = wlm.channel_subset(other, list(range(wl.batch)), list(range(sample.wl.dim)))
+        oracle.vim_dirs(np.stack([sample.u, other.u]), np.stack([sample.delta, other.delta]),
+                        sample.z, np.stack([sample.B, other.B], 1),
+                        np.stack([sample.C, other.C], 1), sample.A, sample.D, sample.dt_bias,
+                        nthreads=threads, zoh=zoh)
     elif conv is None:
-        oracle.run_inputs(sample, nthreads=threads)
+        oracle.run_inputs(sample, nthreads=threads, zoh=zoh)
     else:
         w, b = conv
         ch = list(range(sample.wl.dim))
         oracle.vim_conv(sample.u, w[:, ch], b[:, ch], sample.delta, sample.z, sample.B, sample.C,
-                        sample.A, sample.D, sample.dt_bias, nthreads=threads)
+                        sample.A, sample.D, sample.dt_bias, nthreads=threads, zoh=zoh)
     dt = time.perf_counter() - t0
     cpu = "unknown"
     try:
