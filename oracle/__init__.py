@@ -59,6 +59,10 @@ def _bind(lib):
     lib.oracle_vim_conv_f64.restype = I
     lib.oracle_vim_bidir_grad_f64.argtypes = [I, I, I, Lg] + [P] * 8 + [I] + [P] * 9 + [I]
     lib.oracle_vim_bidir_grad_f64.restype = I
+    lib.oracle_linear_f64.argtypes = [I, I, I, Lg, P, P, P, P, P]
+    lib.oracle_linear_f64.restype = I
+    lib.oracle_dt_proj_f64.argtypes = [I, I, Lg, P, P, P]
+    lib.oracle_dt_proj_f64.restype = I
     return lib
 
 
@@ -225,3 +229,43 @@ def run_inputs(inp, nthreads=None, zoh=False) -> np.ndarray:
                          nthreads=nthreads, zoh=zoh)
     return cross4(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias,
                   wl.H, wl.W, nthreads=nthreads, zoh=zoh)
+
+
+# ---- the linear maps around the scan (x_proj, dt_proj, out_proj)
+def linear(W, x, bias=None, residual=None, lib=None):
+    """nn.Linear in the channel-major layout: out[b, m, t] = sum_k W[m, k]
+    x[b, k, t] + bias[m] (+ residual[b, m, t]). W: [M, K]; x: [batch, K, L]."""
+    lib = lib or load()
+    W, x, bias, residual = map(_f64, (W, x, bias, residual))
+    batch, K, L = x.shape
+    M = W.shape[0]
+    assert W.shape == (M, K) and (bias is None or bias.shape == (M,))
+    assert residual is None or residual.shape == (batch, M, L)
+    out = np.empty((batch, M, L), np.float64)
+    rc = lib.oracle_linear_f64(batch, M, K, L, _ptr(W), _ptr(x), _ptr(bias), _ptr(residual),
+                               _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_linear_f64 failed with status %d" % rc)
+    return out
+
+
+def x_proj(W, u, dstate, lib=None):
+    """SimpleSelectiveSSM.x_proj on u [batch, dim, L] with W [2 dstate + 1, dim]:
+    rows 0..N-1 of the projection are B, rows N..2N-1 are C, row 2N is dt
+    (the code's proj[..., :N], proj[..., N:2N], proj[..., 2N:])."""
+    p = linear(W, u, lib=lib)
+    return p[:, :dstate], p[:, dstate:2 * dstate], p[:, 2 * dstate]
+
+
+def dt_proj(dt, w, lib=None):
+    """dt_proj without its bias (the scan's dt_bias adds it before the
+    softplus): delta_raw[b, d, t] = w[d] dt[b, t]. dt: [batch, L]; w: [dim]."""
+    lib = lib or load()
+    dt, w = _f64(dt), _f64(w)
+    batch, L = dt.shape
+    dim = w.shape[0]
+    out = np.empty((batch, dim, L), np.float64)
+    rc = lib.oracle_dt_proj_f64(batch, dim, L, _ptr(dt), _ptr(w), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_dt_proj_f64 failed with status %d" % rc)
+    return out

@@ -517,3 +517,44 @@ int oracle_vim_bidir_grad_f64(int batch, int dim, int dstate, long L, const doub
     free(jobs); free(th); free(acc);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * The linear maps around the scan. "1. PyTorch Implementation of the
+ * Bidirectional Vision Mamba Block": SimpleSelectiveSSM's x_proj
+ * (Linear(d_model, 2 d_state + 1), no bias) gives B, C and the one-wide dt;
+ * dt_proj (Linear(1, d_model)) widens dt to one value per channel before the
+ * softplus; the block's out_proj (Linear(d_model, d_model)) maps the fused
+ * output, and the residual is added. nn.Linear computes out = in W^T + b; in
+ * the channel-major layout [batch][features][L] used here that is, per
+ * batch row and token t,
+ *     out[b][m][t] = sum_k W[m][k] in[b][k][t] + bias[m] (+ residual[b][m][t]).
+ * W is [M][K] as nn.Linear stores it. bias and residual may be NULL. */
+int oracle_linear_f64(int batch, int M, int K, long L, const double* W, const double* in,
+                      const double* bias, const double* residual, double* out)
+{
+    if (batch < 0 || M < 0 || K < 0 || L < 0) return -1;
+    if (!W || !in || !out) return -1;
+    for (long b = 0; b < batch; ++b)
+        for (long m = 0; m < M; ++m)
+            for (long t = 0; t < L; ++t) {
+                double s = 0.0;
+                for (long k = 0; k < K; ++k) s += W[m * K + k] * in[(b * K + k) * L + t];
+                if (bias) s += bias[m];
+                if (residual) s += residual[(b * M + m) * L + t];
+                out[(b * M + m) * L + t] = s;
+            }
+    return 0;
+}
+
+/* dt_proj with the bias left to the scan (its dt_bias, added before the
+ * softplus): delta_raw[b][d][t] = w[d] dt[b][t], the one-input Linear. */
+int oracle_dt_proj_f64(int batch, int dim, long L, const double* dt, const double* w,
+                       double* delta)
+{
+    if (batch < 0 || dim < 0 || L < 0 || !dt || !w || !delta) return -1;
+    for (long b = 0; b < batch; ++b)
+        for (long d = 0; d < dim; ++d)
+            for (long t = 0; t < L; ++t)
+                delta[(b * dim + d) * L + t] = w[d] * dt[b * L + t];
+    return 0;
+}
