@@ -201,6 +201,44 @@ int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The linear maps around the scan, on the matrix cores (bf16 operands, fp32
+ * accumulation, bf16 results). The guide's block code (section "1. PyTorch
+ * Implementation of the Bidirectional Vision Mamba Block") builds them from
+ * nn.Linear (out = in W^T + b); in the channel-major layout of the scan,
+ * out[b][m][t] = sum_k W[m][k] in[b][k][t]. dtype must be VS_BF16 (VS_F32
+ * returns VS_ERR_UNSUPPORTED). Tensors stay below 2^31 elements. Outputs
+ * must not overlap inputs (VS_ERR_ALIAS) unless stated.
+ */
+
+/* SimpleSelectiveSSM.x_proj (Linear(d_model, 2 dstate + 1), no bias): the
+ * projection's rows 0..N-1 are B, rows N..2N-1 are C and row 2N is dt (the
+ * code's proj[..., :N], proj[..., N:2N], proj[..., 2N:]).
+ *   u     [batch][dim][L] bf16 (the scan's input)
+ *   W     [2 dstate + 1][dim] bf16 (nn.Linear's weight)
+ *   B, C  [batch][dstate][L] bf16, ready for vim_scan_bidir
+ *   dt    [batch][L] fp32 */
+int vim_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+               const void* u, const void* W, void* B, void* C, float* dt, void* stream);
+
+/* dt_proj (Linear(1, d_model)) without its bias, which is the scan's
+ * dt_bias (added inside the softplus): delta_raw[b][d][t] = w[d] dt[b][t].
+ *   dt    [batch][L] fp32; w [dim] fp32 (the weight's only column)
+ *   delta [batch][dim][L] bf16; dim at most 65535 */
+int vim_dt_proj(int64_t batch, int64_t dim, int64_t seqlen, int dtype, const float* dt,
+                const float* w, void* delta, void* stream);
+
+/* The block's out_proj (Linear(d_model, d_model) in the guide; any shape
+ * here) plus the residual:
+ *   out[b][m][t] = sum_k W[m][k] y[b][k][t] + bias[m] + residual[b][m][t]
+ *   y        [batch][dim_in][L] bf16; W [dim_out][dim_in] bf16
+ *   bias     [dim_out] fp32 or NULL; residual [batch][dim_out][L] bf16 or NULL
+ *   out      [batch][dim_out][L] bf16; it may be the residual itself
+ *            (in place), but no other overlap is allowed */
+int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen, int dtype,
+                 const void* y, const void* W, const float* bias, const void* residual, void* out,
+                 void* stream);
+
+/*
  * VMamba four-direction cross-scan of an H x W grid (L = H*W tokens, stored
  * row-major: token p = i*W + j). Direction 0 visits p = t, 1 visits
  * p = L-1-t, 2 visits the columns top to bottom, left to right

@@ -144,6 +144,34 @@ def test_flag_validation(nat):
              fake(13), fake(14), fake(15), need, None) == -6
 
 
+def test_projection_validation(nat):
+    """Every call below fails validation, so no kernel is launched."""
+    x, o = nat.lib.vim_x_proj, nat.lib.vim_out_proj
+    xp = lambda **k: x(k.get("batch", 2), k.get("dim", 64), k.get("N", 16), k.get("L", 37),
+                       k.get("dtype", nat.VS_BF16), k.get("u", fake(0)), k.get("W", fake(1)),
+                       k.get("B", fake(2)), k.get("C", fake(3)), k.get("dt", fake(4)), None)
+    assert xp(dtype=nat.VS_F32) == -6           # bf16 only
+    assert xp(dtype=5) == -3
+    assert xp(N=17) == -6
+    assert xp(N=0) == -2
+    assert xp(u=None) == -1
+    assert xp(dt=fake(4) + 2) == -4             # fp32 dt misaligned
+    assert xp(B=fake(0) + 64) == -5             # B inside u
+    assert xp(C=fake(2) + 64) == -5             # C overlaps B
+    op = lambda **k: o(k.get("batch", 2), 64, 48, 37, k.get("dtype", nat.VS_BF16),
+                       k.get("y", fake(0)), k.get("W", fake(1)), k.get("bias", None),
+                       k.get("res", None), k.get("out", fake(3)), None)
+    assert op(dtype=nat.VS_F32) == -6
+    assert op(W=None) == -1
+    assert op(out=fake(0) + 2) == -5            # out inside y
+    assert op(res=fake(3) + 2) == -5            # partial overlap with the residual
+    assert op(batch=0) == -2
+    d = nat.lib.vim_dt_proj
+    assert d(2, 8, 37, nat.VS_F32, fake(0), fake(1), fake(2), None) == -6
+    assert d(2, 70000, 37, nat.VS_BF16, fake(0), fake(1), fake(2), None) == -6
+    assert d(2, 8, 37, nat.VS_BF16, fake(0), fake(1), fake(0) + 8, None) == -5
+
+
 def test_cross4_validation(nat):
     f = nat.lib.vmamba_cross_scan4
     args = [fake(0), fake(1), None, fake(3), fake(4), fake(5), None, None, 1, fake(8), fake(9),

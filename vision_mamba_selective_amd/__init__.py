@@ -8,7 +8,8 @@ library.
 """
 
 __all__ = ["vim_scan_bidir", "vim_scan_bidir_dirs", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
-           "vmamba_cross_scan4", "s6_scan_1d", "workspace_bytes"]
+           "vmamba_cross_scan4", "s6_scan_1d", "workspace_bytes", "vim_x_proj", "vim_dt_proj",
+           "vim_out_proj"]
 
 
 def __getattr__(name):

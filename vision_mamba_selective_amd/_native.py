@@ -35,6 +35,9 @@ SIGNATURES = {
                                 _P, _I, _P, _P, _SZ, _P]),
     "s6_scan_1d": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                         _P, _P]),
+    "vim_x_proj": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P]),
+    "vim_dt_proj": (_I, [_I64, _I64, _I64, _I, _P, _P, _P, _P]),
+    "vim_out_proj": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P]),
     "vs_strerror": (ctypes.c_char_p, [_I]),
     "vs_last_error": (ctypes.c_char_p, []),
     "vs_abi_version": (_I, []),

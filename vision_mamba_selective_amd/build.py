@@ -8,6 +8,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "vimscan.hip")
+SRCS = [SRC, os.path.join(PKG, "csrc", "proj.hip")]
 LIB = os.path.join(PKG, "libvimscan.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -27,7 +28,7 @@ def hipcc() -> str:
 
 def build(out: str = LIB, extra=()) -> str:
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, *SRCS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)

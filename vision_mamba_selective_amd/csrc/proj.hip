@@ -1,0 +1,341 @@
+// proj.hip -- the linear maps around the scan, on gfx950 matrix cores.
+//
+// "Vision Mamba Guide: Efficient Bidirectional SSM & VMamba", section
+// "1. PyTorch Implementation of the Bidirectional Vision Mamba Block":
+// SimpleSelectiveSSM's x_proj (Linear(d_model, 2 d_state + 1), no bias)
+// produces B, C and a one-wide dt; dt_proj (Linear(1, d_model)) widens dt
+// per channel inside the softplus; the block's out_proj (Linear(d_model,
+// d_model)) maps the fused output before the residual is added. In the
+// channel-major layout [batch][features][L] of the scan, nn.Linear's
+// out = in W^T + b is, for every batch row b and token t,
+//     out[b][m][t] = sum_k W[m][k] in[b][k][t] (+ bias[m]) (+ residual[b][m][t]).
+//
+// proj_gemm_kernel computes one batch row's Out[M][L] = W[M][K] X[K][L] in
+// BM x BN tiles with v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
+// accumulation). Per 32-deep slice of K, W's rows are copied to LDS as they
+// are (k contiguous) and X's columns are gathered one per thread so that LDS
+// holds them k-contiguous too: the MFMA takes 8 consecutive k of one row
+// (A) and of one column (B) per lane. The next slice is loaded into
+// registers while the matrix cores work on the current one. Four waves in a
+// 2 x 2 grid each own (BM/2) x (BN/2) of the tile.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vimscan.h"
+#include "vs_internal.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kThreads = 256;
+constexpr int kBK = 32;                 // K per LDS slice
+constexpr int kRow = kBK + 8;           // LDS row: 32 bf16 + 8 padding (80 bytes)
+
+enum { kEpiOut = 0, kEpiXproj = 1 };
+
+struct ProjArgs {
+    const uint16_t* W;     // [M][K] bf16
+    const uint16_t* X;     // [batch][K][L] bf16
+    const float* bias;     // [M] fp32 or null
+    const uint16_t* res;   // [batch][M][L] bf16 or null
+    uint16_t* out;         // kEpiOut: [batch][M][L] bf16
+    uint16_t* B;           // kEpiXproj: rows 0..N-1 -> B [batch][N][L]
+    uint16_t* C;           //            rows N..2N-1 -> C [batch][N][L]
+    float* dt;             //            row 2N -> dt [batch][L] (fp32)
+    int M, K, N, L;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
+}
+
+template <int BM, int BN, int EPI, bool WVEC>
+__global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
+    static_assert(BM % 64 == 0 && BN % 64 == 0, "2 x 2 waves of 32 x 32 MFMA tiles");
+    constexpr int TM = BM / 64, TN = BN / 64;
+    // X slice: each column of BN is gathered by kThreads / BN threads, KPT k each
+    constexpr int kColThreads = kThreads / BN;
+    constexpr int KPT = kBK / kColThreads;
+    static_assert(KPT % 8 == 0, "whole 16-byte LDS rows");
+    // W slice: 16-byte chunks (WVEC) or single elements
+    constexpr int kChunks = BM * kBK / 8;
+    constexpr int kChunkPT = (kChunks + kThreads - 1) / kThreads;
+    constexpr int kElemPT = BM * kBK / kThreads;
+
+    __shared__ __attribute__((aligned(16))) uint16_t sA[BM][kRow];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[BN][kRow];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+    const int64_t b = blockIdx.z;
+    const int M = a.M, K = a.K, L = a.L;
+    const uint16_t* __restrict__ Xb = a.X + b * static_cast<int64_t>(K) * L;
+
+    // this thread's X column (clamped: columns past L feed only masked outputs)
+    const int xn = tid % BN, xk = (tid / BN) * KPT;
+    const int64_t xcol = n0 + xn < L ? n0 + xn : L - 1;
+
+    uint4 wreg[WVEC ? kChunkPT : 1];
+    uint16_t wel[WVEC ? 1 : kElemPT];
+    uint16_t xreg[KPT];
+    auto load_slice = [&](int k0) {
+        if (WVEC) {
+#pragma unroll
+            for (int i = 0; i < kChunkPT; ++i) {
+                const int c = tid + i * kThreads;
+                const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (c < kChunks && m0 + r < M && k0 + kc < K)
+                    v = *reinterpret_cast<const uint4*>(a.W + static_cast<int64_t>(m0 + r) * K + k0 + kc);
+                wreg[i] = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kElemPT; ++i) {
+                const int e = tid + i * kThreads;
+                const int r = e / kBK, kk = e % kBK;
+                wel[i] = (m0 + r < M && k0 + kk < K) ? a.W[static_cast<int64_t>(m0 + r) * K + k0 + kk] : 0;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int k = k0 + xk + j;
+            // rows past K: any finite value (W is zero there)
+            xreg[j] = Xb[static_cast<int64_t>(k < K ? k : K - 1) * L + xcol];
+        }
+    };
+    auto store_slice = [&]() {
+        if (WVEC) {
+#pragma unroll
+            for (int i = 0; i < kChunkPT; ++i) {
+                const int c = tid + i * kThreads;
+                if (c < kChunks)
+                    *reinterpret_cast<uint4*>(&sA[c / (kBK / 8)][(c % (kBK / 8)) * 8]) = wreg[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kElemPT; ++i) {
+                const int e = tid + i * kThreads;
+                sA[e / kBK][e % kBK] = wel[i];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < KPT / 8; ++q) {
+            uint4 v;
+            v.x = xreg[8 * q] | (uint32_t(xreg[8 * q + 1]) << 16);
+            v.y = xreg[8 * q + 2] | (uint32_t(xreg[8 * q + 3]) << 16);
+            v.z = xreg[8 * q + 4] | (uint32_t(xreg[8 * q + 5]) << 16);
+            v.w = xreg[8 * q + 6] | (uint32_t(xreg[8 * q + 7]) << 16);
+            *reinterpret_cast<uint4*>(&sB[xn][xk + 8 * q]) = v;
+        }
+    };
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int fr = lane & 31, fk = 8 * (lane >> 5);     // fragment row / column, k offset
+    load_slice(0);
+    for (int k0 = 0; k0 < K; k0 += kBK) {
+        store_slice();
+        __syncthreads();
+        if (k0 + kBK < K) load_slice(k0 + kBK);
+#pragma unroll
+        for (int ks = 0; ks < kBK; ks += 16) {
+            bf16x8 fa[TM], fb[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                fa[i] = *reinterpret_cast<const bf16x8*>(&sA[wm * (BM / 2) + i * 32 + fr][ks + fk]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8*>(&sB[wn * (BN / 2) + j * 32 + fr][ks + fk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // accumulator r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int n = n0 + wn * (BN / 2) + j * 32 + fr;
+            if (n >= L) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (m >= M) continue;
+                float v = acc[i][j][r];
+                if (EPI == kEpiOut) {
+                    const int64_t o = (b * M + m) * static_cast<int64_t>(L) + n;
+                    if (a.bias) v += a.bias[m];
+                    if (a.res) v += bf16_to_f32(a.res[o]);
+                    a.out[o] = f32_to_bf16(v);
+                } else {
+                    const int N = a.N;
+                    if (m < N)
+                        a.B[(b * N + m) * static_cast<int64_t>(L) + n] = f32_to_bf16(v);
+                    else if (m < 2 * N)
+                        a.C[(b * N + (m - N)) * static_cast<int64_t>(L) + n] = f32_to_bf16(v);
+                    else
+                        a.dt[b * L + n] = v;
+                }
+            }
+        }
+}
+
+// dt_proj without its bias: delta[b][d][t] = w[d] dt[b][t], in bf16.
+__global__ __launch_bounds__(kThreads) void dt_proj_kernel(const float* __restrict__ dt,
+                                                           const float* __restrict__ w,
+                                                           uint16_t* __restrict__ delta, int dim,
+                                                           int L) {
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    if (t >= L) return;
+    const int d = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    delta[(b * dim + d) * static_cast<int64_t>(L) + t] = f32_to_bf16(w[d] * dt[b * L + t]);
+}
+
+bool overlap(const void* p, size_t np, const void* q, size_t nq) {
+    if (!p || !q || np == 0 || nq == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
+    return a0 < b0 + nq && b0 < a0 + np;
+}
+bool al(const void* p, size_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
+
+int check_sizes(int64_t batch, int64_t M, int64_t K, int64_t L) {
+    if (batch < 1 || M < 1 || K < 1 || L < 1)
+        return vs_internal_fail(VS_ERR_SHAPE, "batch, feature counts and the sequence length must be >= 1");
+    if (batch > 65535) return vs_internal_fail(VS_ERR_SHAPE, "batch above 65535 is not supported");
+    if (M * K >= (int64_t(1) << 31) || batch * K * L >= (int64_t(1) << 31) ||
+        batch * M * L >= (int64_t(1) << 31) || L >= (int64_t(1) << 30))
+        return vs_internal_fail(VS_ERR_UNSUPPORTED, "tensors of 2^31 elements or more are not supported");
+    return VS_OK;
+}
+
+template <int BM, int BN, int EPI>
+int launch(const ProjArgs& a, int64_t batch, hipStream_t st) {
+    const int64_t tiles_l = (static_cast<int64_t>(a.L) + BN - 1) / BN;
+    if (tiles_l > 65535)
+        return vs_internal_fail(VS_ERR_UNSUPPORTED, "sequence too long for the projection grid");
+    const dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>(tiles_l),
+                    static_cast<unsigned>(batch));
+    const bool wvec = a.K % 8 == 0 && al(a.W, 16);
+    if (wvec)
+        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, EPI, true>), grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, EPI, false>), grid, dim3(kThreads), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_internal_fail(VS_ERR_HIP, hipGetErrorString(e));
+    return VS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vim_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+               const void* u, const void* W, void* B, void* C, float* dt, void* stream) {
+    vs_internal_clear_error();
+    if (dtype != VS_BF16)
+        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
+                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
+    if (dstate < 1 || dstate > VS_MAX_DSTATE)
+        return vs_internal_fail(dstate < 1 ? VS_ERR_SHAPE : VS_ERR_UNSUPPORTED, "dstate must be in 1..16");
+    const int64_t M = 2 * dstate + 1;
+    int rc = check_sizes(batch, M, dim, seqlen);
+    if (rc != VS_OK) return rc;
+    if (!u || !W || !B || !C || !dt) return vs_internal_fail(VS_ERR_NULL, "u, W, B, C and dt must not be NULL");
+    if (!al(u, 2) || !al(W, 2) || !al(B, 2) || !al(C, 2) || !al(dt, 4))
+        return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
+    const size_t nu = static_cast<size_t>(batch * dim * seqlen) * 2, nw = static_cast<size_t>(M * dim) * 2;
+    const size_t nbc = static_cast<size_t>(batch * dstate * seqlen) * 2, ndt = static_cast<size_t>(batch * seqlen) * 4;
+    const void* outs[] = {B, C, dt};
+    const size_t out_b[] = {nbc, nbc, ndt};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], out_b[i], u, nu) || overlap(outs[i], out_b[i], W, nw))
+            return vs_internal_fail(VS_ERR_ALIAS, "an output overlaps an input");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], out_b[i], outs[j], out_b[j]))
+                return vs_internal_fail(VS_ERR_ALIAS, "outputs overlap each other");
+    }
+    ProjArgs a{};
+    a.W = static_cast<const uint16_t*>(W);
+    a.X = static_cast<const uint16_t*>(u);
+    a.B = static_cast<uint16_t*>(B);
+    a.C = static_cast<uint16_t*>(C);
+    a.dt = dt;
+    a.M = static_cast<int>(M); a.K = static_cast<int>(dim);
+    a.N = static_cast<int>(dstate); a.L = static_cast<int>(seqlen);
+    return launch<64, 64, kEpiXproj>(a, batch, static_cast<hipStream_t>(stream));
+}
+
+int vim_dt_proj(int64_t batch, int64_t dim, int64_t seqlen, int dtype, const float* dt,
+                const float* w, void* delta, void* stream) {
+    vs_internal_clear_error();
+    if (dtype != VS_BF16)
+        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
+                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
+    int rc = check_sizes(batch, dim, 1, seqlen);
+    if (rc != VS_OK) return rc;
+    if (dim > 65535) return vs_internal_fail(VS_ERR_UNSUPPORTED, "dim above 65535 is not supported");
+    if (!dt || !w || !delta) return vs_internal_fail(VS_ERR_NULL, "dt, w and delta must not be NULL");
+    if (!al(dt, 4) || !al(w, 4) || !al(delta, 2)) return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
+    const size_t nd = static_cast<size_t>(batch * dim * seqlen) * 2;
+    if (overlap(delta, nd, dt, static_cast<size_t>(batch * seqlen) * 4) ||
+        overlap(delta, nd, w, static_cast<size_t>(dim) * 4))
+        return vs_internal_fail(VS_ERR_ALIAS, "delta overlaps an input");
+    const dim3 grid(static_cast<unsigned>((seqlen + kThreads - 1) / kThreads), static_cast<unsigned>(dim),
+                    static_cast<unsigned>(batch));
+    hipLaunchKernelGGL(dt_proj_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), dt, w,
+                       static_cast<uint16_t*>(delta), static_cast<int>(dim), static_cast<int>(seqlen));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return vs_internal_fail(VS_ERR_HIP, hipGetErrorString(e));
+    return VS_OK;
+}
+
+int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen, int dtype,
+                 const void* y, const void* W, const float* bias, const void* residual, void* out,
+                 void* stream) {
+    vs_internal_clear_error();
+    if (dtype != VS_BF16)
+        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
+                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
+    int rc = check_sizes(batch, dim_out, dim_in, seqlen);
+    if (rc != VS_OK) return rc;
+    if (!y || !W || !out) return vs_internal_fail(VS_ERR_NULL, "y, W and out must not be NULL");
+    if (!al(y, 2) || !al(W, 2) || !al(out, 2) || !al(residual, 2) || !al(bias, 4))
+        return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
+    const size_t no = static_cast<size_t>(batch * dim_out * seqlen) * 2;
+    if (overlap(out, no, y, static_cast<size_t>(batch * dim_in * seqlen) * 2) ||
+        overlap(out, no, W, static_cast<size_t>(dim_out * dim_in) * 2) ||
+        overlap(out, no, bias, static_cast<size_t>(dim_out) * 4))
+        return vs_internal_fail(VS_ERR_ALIAS, "out overlaps an input");
+    // out may be the residual itself (each element is read before it is
+    // written, by the same thread); any other overlap is refused
+    if (residual != out && overlap(out, no, residual, no))
+        return vs_internal_fail(VS_ERR_ALIAS, "out partly overlaps the residual");
+    ProjArgs a{};
+    a.W = static_cast<const uint16_t*>(W);
+    a.X = static_cast<const uint16_t*>(y);
+    a.bias = bias;
+    a.res = static_cast<const uint16_t*>(residual);
+    a.out = static_cast<uint16_t*>(out);
+    a.M = static_cast<int>(dim_out); a.K = static_cast<int>(dim_in); a.L = static_cast<int>(seqlen);
+    return launch<128, 128, kEpiOut>(a, batch, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "vimscan.h"
+#include "vs_internal.h"
 
 namespace {
 
@@ -1384,6 +1385,10 @@ int run(Call c) {
 }
 
 }  // namespace
+
+// the error record, for the projection kernels' translation unit
+int vs_internal_fail(int code, const char* msg) { return fail(code, msg); }
+void vs_internal_clear_error() { g_last_error.clear(); }
 
 // ---------------------------------------------------------------- C ABI
 extern "C" {

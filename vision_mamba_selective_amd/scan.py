@@ -254,3 +254,60 @@ def s6_scan_1d(u, delta, z, B, C, A, Dskip=None, dt_bias=None, reverse=False,
                             _ptr(dt_bias), _flags(delta_softplus, zoh), _ptr(y), _stream(dev))
     nat.check("s6_scan_1d", rc)
     return y
+
+
+# ---- the linear maps around the scan (bf16, matrix cores)
+def _bf16_act(name, t, shape, dev):
+    _act(name, t, shape, torch.bfloat16, dev)
+
+
+def vim_x_proj(u, W, dstate):
+    """SimpleSelectiveSSM.x_proj: u [batch, dim, L] bf16, W [2 dstate + 1, dim]
+    bf16 -> (B [batch, dstate, L] bf16, C [batch, dstate, L] bf16,
+    dt [batch, L] fp32)."""
+    batch, dim, L = u.shape
+    dev = u.device
+    _bf16_act("u", u, (batch, dim, L), dev)
+    _bf16_act("W", W, (2 * dstate + 1, dim), dev)
+    B = torch.empty(batch, dstate, L, dtype=torch.bfloat16, device=dev)
+    C = torch.empty_like(B)
+    dt = torch.empty(batch, L, dtype=torch.float32, device=dev)
+    rc = nat.lib.vim_x_proj(batch, dim, dstate, L, nat.VS_BF16, _ptr(u), _ptr(W), _ptr(B), _ptr(C),
+                            _ptr(dt), _stream(dev))
+    nat.check("vim_x_proj", rc)
+    return B, C, dt
+
+
+def vim_dt_proj(dt, w):
+    """dt_proj without its bias (the scan's dt_bias): dt [batch, L] fp32,
+    w [dim] fp32 -> delta_raw [batch, dim, L] bf16."""
+    batch, L = dt.shape
+    dim = w.shape[0]
+    dev = dt.device
+    _act("dt", dt, (batch, L), torch.float32, dev)
+    _act("w", w, (dim,), torch.float32, dev)
+    delta = torch.empty(batch, dim, L, dtype=torch.bfloat16, device=dev)
+    rc = nat.lib.vim_dt_proj(batch, dim, L, nat.VS_BF16, _ptr(dt), _ptr(w), _ptr(delta),
+                             _stream(dev))
+    nat.check("vim_dt_proj", rc)
+    return delta
+
+
+def vim_out_proj(y, W, bias=None, residual=None, out=None):
+    """out = W y + bias + residual: y [batch, dim_in, L] bf16, W [dim_out,
+    dim_in] bf16, bias [dim_out] fp32 or None, residual [batch, dim_out, L]
+    bf16 or None; out may be the residual (in place)."""
+    batch, dim_in, L = y.shape
+    dim_out = W.shape[0]
+    dev = y.device
+    _bf16_act("y", y, (batch, dim_in, L), dev)
+    _bf16_act("W", W, (dim_out, dim_in), dev)
+    _param("bias", bias, (dim_out,), dev)
+    if residual is not None:
+        _bf16_act("residual", residual, (batch, dim_out, L), dev)
+    o = torch.empty(batch, dim_out, L, dtype=torch.bfloat16, device=dev) if out is None else out
+    _bf16_act("out", o, (batch, dim_out, L), dev)
+    rc = nat.lib.vim_out_proj(batch, dim_in, dim_out, L, nat.VS_BF16, _ptr(y), _ptr(W),
+                              _ptr(bias), _ptr(residual), _ptr(o), _stream(dev))
+    nat.check("vim_out_proj", rc)
+    return o
