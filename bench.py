@@ -35,8 +35,12 @@ FP32_LANE_OPS = CU * 128 * CLOCK_HZ       # 157.3 TFLOP/s fp32 vector = 78.6 T l
 SLOTS_PER_UPDATE = 8
 UPDATE_PEAK = FP32_LANE_OPS / SLOTS_PER_UPDATE   # 9.83e12 state updates / s
 
+#: dense bf16 matrix-core peak (no sparsity)
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "vision_mamba_selective_amd", "csrc", "vimscan.hip")
+PROJ_SRC = os.path.join(ROOT, "vision_mamba_selective_amd", "csrc", "proj.hip")
 
 
 def parse():
@@ -63,13 +67,17 @@ def parse():
     p.add_argument("--dirs", action="store_true",
                    help="time vim_scan_bidir_dirs: per-direction u, delta, B and C (a second "
                         "seeded draw feeds the backward direction)")
+    p.add_argument("--proj", action="store_true",
+                   help="time the projections around the scan at the workload's shape: one step is "
+                        "out_proj (dim -> dim, bias + residual) on the matrix cores; x_proj and "
+                        "dt_proj are timed beside it")
     p.add_argument("--copy-probe", action="store_true",
                    help="instead of the scan, run torch copies of known size (counter scale)")
     return p.parse_args()
 
 
-def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
+def kernel_hash(path=KERNEL_SRC):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
@@ -93,6 +101,8 @@ def main():
 
     if args.copy_probe:
         return copy_probe(torch, dev)
+    if args.proj:
+        return proj_bench(args, torch, dev)
 
     import vision_mamba_selective_amd as vms
 
@@ -327,6 +337,129 @@ def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False):
     return {"value": round(sample.wl.tokens_channels / dt / 1e9, 5), "unit": "Gtoken*ch/s",
             "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
             "sample": desc + ", fp64, " + cpu + ", " + platform.machine()}
+
+
+def proj_bench(args, torch, dev):
+    """The projections at the workload's shape. One step is out_proj: y
+    [batch, dim, L] -> W [dim, dim] y + bias + residual (bf16, matrix cores);
+    x_proj (dim -> 2 dstate + 1) and dt_proj are timed beside it."""
+    import numpy as np
+    import vision_mamba_selective_amd as vms
+    from vision_mamba_selective_amd import workloads as wlm
+
+    idx = wlm.HEADLINE if args.workload is None else args.workload
+    wl = wlm.WORKLOADS[idx]
+    if wl.kind != "vim" or wl.dtype != wlm.BF16:
+        print("--proj applies to the bf16 Vim workloads", file=sys.stderr)
+        sys.exit(2)
+    print("bench: projections at %s" % wl.name, file=sys.stderr, flush=True)
+    rng = np.random.default_rng(wl.seed + 700)
+    bf = torch.bfloat16
+    dim, L, batch, N = wl.dim, wl.seqlen, wl.batch, wl.dstate
+
+    def w(shape, scale):
+        return torch.from_numpy(wlm.round_bf16(scale * rng.standard_normal(shape))).to(dev).to(bf)
+
+    Wo, Wx = w((dim, dim), dim ** -0.5), w((2 * N + 1, dim), dim ** -0.5)
+    bias = torch.from_numpy(rng.standard_normal(dim).astype(np.float32)).to(dev)
+    wdt = torch.from_numpy(rng.standard_normal(dim).astype(np.float32)).to(dev)
+    y0 = w((batch, dim, L), 1.0)
+    r0 = w((batch, dim, L), 1.0)
+    per_set = 3 * y0.numel() * 2
+    nsets = args.sets or max(1, int(np.ceil(768e6 / per_set)))
+    sets = [dict(y=y0 if s == 0 else y0.clone(), r=r0 if s == 0 else r0.clone(),
+                 o=torch.empty_like(y0)) for s in range(nsets)]
+
+    def step(t):
+        vms.vim_out_proj(t["y"], Wo, bias, t["r"], out=t["o"])
+
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, n):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+    print("bench: warmup done, timing %d steps over %d input sets" % (args.steps, nsets),
+          file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    kern_ms = timed(lambda i: step(sets[i % nsets]), args.steps)
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    # x_proj and dt_proj, each timed on its own
+    x_ms = timed(lambda i: vms.vim_x_proj(sets[i % nsets]["y"], Wx, N), args.steps)
+    _, _, dt = vms.vim_x_proj(y0, Wx, N)
+    d_ms = timed(lambda i: vms.vim_dt_proj(dt, wdt), args.steps)
+
+    flops = 2.0 * batch * dim * dim * L
+    tflops = flops / (kern_ms * 1e-3) / 1e12
+    alg_bytes = 3 * batch * dim * L * 2 + dim * dim * 2 + dim * 4   # y, residual, out, W, bias
+    hbm_gbs = alg_bytes / (kern_ms * 1e-3) / 1e9
+    tc = batch * dim * L
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        try:
+            with open(PROFILE_TRAFFIC) as f:
+                rec = json.load(f).get(wl.name + "+proj")
+            if rec and rec.get("kernel_sha") == kernel_hash(PROJ_SRC):
+                traffic = rec.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    out = {
+        "metric": "selective-scan Gtoken*ch/s + achieved HBM GB/s (Vim-S, 1024^2, bidir)",
+        "value": round(tc / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtoken*ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "kind": "vim", "batch": batch, "d_inner": dim,
+                   "d_state": N, "seq_len": L,
+                   "pass": "out_proj %d->%d + bias + residual (matrix cores)" % (dim, dim)},
+        "kernel_ms": round(kern_ms, 5),
+        "x_proj_ms": round(x_ms, 5),
+        "dt_proj_ms": round(d_ms, 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+        "roofline_hbm": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": alg_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = proj_cpu_baseline(sets[0]["y"], Wo, bias, sets[0]["r"])
+    print(json.dumps(out), flush=True)
+
+
+def proj_cpu_baseline(y, W, bias, r, tokens=256):
+    """The fp64 oracle's linear map (single-threaded loops) on every batch row
+    and the first `tokens` tokens of out_proj."""
+    import oracle
+    ys = y[:, :, :tokens].float().cpu().numpy()
+    rs = r[:, :, :tokens].float().cpu().numpy()
+    Wn, bn = W.float().cpu().numpy(), bias.cpu().numpy()
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.linear(Wn, ys, bn, rs)
+    dt = time.perf_counter() - t0
+    tc = ys.shape[0] * W.shape[0] * ys.shape[2]
+    return {"value": round(tc / dt / 1e9, 6), "unit": "Gtoken*ch/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "out_proj on %d batch rows x %d tokens, fp64, %s" % (
+                ys.shape[0], ys.shape[2], platform.machine())}
 
 
 def copy_probe(torch, dev):

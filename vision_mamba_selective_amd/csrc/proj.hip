@@ -17,7 +17,11 @@
 // holds them k-contiguous too: the MFMA takes 8 consecutive k of one row
 // (A) and of one column (B) per lane. The next slice is loaded into
 // registers while the matrix cores work on the current one. Four waves in a
-// 2 x 2 grid each own (BM/2) x (BN/2) of the tile.
+// 2 x 2 grid each own (BM/2) x (BN/2) of the tile. out_proj's epilogue stages
+// the tile through LDS, so that the residual is read and the result written
+// in whole rows. Measured at Vim-S 1024^2 (768 -> 768, 8 x 4,097 tokens):
+// 128 x 64 tiles beat 128 x 128 and 64 x 128 (more workgroups per CU hide
+// more of the global-load latency, which bounds this kernel).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -31,8 +35,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;                 // K per LDS slice
-constexpr int kRow = kBK + 8;           // LDS row: 32 bf16 + 8 padding (80 bytes)
+constexpr int kBK = 64;                 // K per LDS slice
+constexpr int kRow = kBK + 8;           // LDS row: 64 bf16 + 8 padding (144 bytes)
 
 enum { kEpiOut = 0, kEpiXproj = 1 };
 
@@ -66,8 +70,16 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     constexpr int kChunkPT = (kChunks + kThreads - 1) / kThreads;
     constexpr int kElemPT = BM * kBK / kThreads;
 
-    __shared__ __attribute__((aligned(16))) uint16_t sA[BM][kRow];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[BN][kRow];
+    // the operand slices; after the K loop the same memory holds the output
+    // tile (bf16, rows of BN + 8), staged so that residual reads and result
+    // writes move whole rows of the tile
+    constexpr int kOutRow = BN + 8;
+    constexpr int kSmem = (BM + BN) * kRow > BM * kOutRow ? (BM + BN) * kRow : BM * kOutRow;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
+    __shared__ float sBias[BM];
+    uint16_t (*sA)[kRow] = reinterpret_cast<uint16_t (*)[kRow]>(smem);
+    uint16_t (*sB)[kRow] = reinterpret_cast<uint16_t (*)[kRow]>(smem + BM * kRow);
+    uint16_t (*sT)[kOutRow] = reinterpret_cast<uint16_t (*)[kOutRow]>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -143,6 +155,8 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    if (EPI == kEpiOut && tid < BM)
+        sBias[tid] = (a.bias && m0 + tid < M) ? a.bias[m0 + tid] : 0.f;
     const int fr = lane & 31, fk = 8 * (lane >> 5);     // fragment row / column, k offset
     load_slice(0);
     for (int k0 = 0; k0 < K; k0 += kBK) {
@@ -168,24 +182,60 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     }
 
     // accumulator r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+    if (EPI == kEpiOut) {
+        // 1. the residual tile into LDS, whole rows per instruction (rows and
+        //    columns past the matrix: any valid element, never stored)
+        constexpr int kRowsPT = BM * BN / kThreads;         // rows per thread
+        const int tn = tid % BN, tr0 = tid / BN;
+        constexpr int kRowStep = kThreads / BN;
+        const int64_t ncl = n0 + tn < L ? n0 + tn : L - 1;
+        if (a.res) {
+#pragma unroll 16
+            for (int q = 0; q < kRowsPT; ++q) {
+                const int row = tr0 + q * kRowStep;
+                const int64_t mcl = m0 + row < M ? m0 + row : M - 1;
+                sT[row][tn] = a.res[(b * M + mcl) * static_cast<int64_t>(L) + ncl];
+            }
+        }
+        __syncthreads();
+        // 2. each lane finishes its own elements in place: acc + bias + residual
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n0 + wn * (BN / 2) + j * 32 + fr;
-            if (n >= L) continue;
+            for (int j = 0; j < TN; ++j) {
+                const int cn = wn * (BN / 2) + j * 32 + fr;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                if (m >= M) continue;
-                float v = acc[i][j][r];
-                if (EPI == kEpiOut) {
-                    const int64_t o = (b * M + m) * static_cast<int64_t>(L) + n;
-                    if (a.bias) v += a.bias[m];
-                    if (a.res) v += bf16_to_f32(a.res[o]);
-                    a.out[o] = f32_to_bf16(v);
-                } else {
-                    const int N = a.N;
+                for (int r = 0; r < 16; ++r) {
+                    const int cm = wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    float v = acc[i][j][r] + sBias[cm];
+                    if (a.res) v += bf16_to_f32(sT[cm][cn]);
+                    sT[cm][cn] = f32_to_bf16(v);
+                }
+            }
+        __syncthreads();
+        // 3. whole rows out
+        if (n0 + tn < L) {
+#pragma unroll 16
+            for (int q = 0; q < kRowsPT; ++q) {
+                const int row = tr0 + q * kRowStep;
+                if (m0 + row < M)
+                    a.out[(b * M + m0 + row) * static_cast<int64_t>(L) + n0 + tn] = sT[row][tn];
+            }
+        }
+    } else {
+        // x_proj: rows 0..N-1 -> B, N..2N-1 -> C (bf16), row 2N -> dt (fp32)
+        const int N = a.N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int n = n0 + wn * (BN / 2) + j * 32 + fr;
+                if (n >= L) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (m >= M) continue;
+                    const float v = acc[i][j][r];
                     if (m < N)
                         a.B[(b * N + m) * static_cast<int64_t>(L) + n] = f32_to_bf16(v);
                     else if (m < 2 * N)
@@ -194,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
                         a.dt[b * L + n] = v;
                 }
             }
-        }
+    }
 }
 
 // dt_proj without its bias: delta[b][d][t] = w[d] dt[b][t], in bf16.
@@ -335,7 +385,7 @@ int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen,
     a.res = static_cast<const uint16_t*>(residual);
     a.out = static_cast<uint16_t*>(out);
     a.M = static_cast<int>(dim_out); a.K = static_cast<int>(dim_in); a.L = static_cast<int>(seqlen);
-    return launch<128, 128, kEpiOut>(a, batch, static_cast<hipStream_t>(stream));
+    return launch<128, 64, kEpiOut>(a, batch, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"
