@@ -83,8 +83,24 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-    const int64_t b = blockIdx.z;
+    // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by
+    // linear id; renumber them so that each XCD runs one contiguous range of
+    // tiles. Neighbouring M tiles read the same X columns, which then stay
+    // in that XCD's L2 instead of being fetched from HBM once per tile.
+    uint32_t mt, nt, bt;
+    {
+        constexpr uint32_t kXcds = 8;
+        const uint32_t gx = gridDim.x, gy = gridDim.y;
+        const uint32_t G = gx * gy * gridDim.z;
+        const uint32_t lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+        const uint32_t x = lin % kXcds, k = lin / kXcds, q = G / kXcds, r = G % kXcds;
+        const uint32_t v = x * q + (x < r ? x : r) + k;
+        mt = v % gx;
+        nt = (v / gx) % gy;
+        bt = v / (gx * gy);
+    }
+    const int m0 = mt * BM, n0 = nt * BN;
+    const int64_t b = bt;
     const int M = a.M, K = a.K, L = a.L;
     const uint16_t* __restrict__ Xb = a.X + b * static_cast<int64_t>(K) * L;
 
