@@ -45,6 +45,9 @@ constexpr int kRowLanes = 16;       // one recurrence per DPP row
 constexpr int kBlockTok = 16;       // tokens per block step
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kTilePad = 20;        // LDS row stride (floats) of a 16-token tile
+constexpr int kPairTok = 32;        // tokens per B/C tile of the forward scan (two blocks)
+constexpr int kPairPad = 36;        // its LDS row stride (floats): conflict-free b128 rows
+constexpr int kTokAhead = 3;        // blocks the forward scan's token loads run ahead
 constexpr int kTr = 32;             // grid transpose tile edge
 constexpr int kTrPad = kTr + 1;
 
@@ -162,22 +165,16 @@ __device__ __forceinline__ float row_transpose_sum(const float (&c)[16], int lan
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// softplus(x) = max(x, 0) + log1p(w), w = e^{-|x|} in (0, 1].
-// log1p(w) = 2 atanh(r) with r = w / (2 + w) in (0, 1/3], summed as the odd
-// series 2 (r + r^3/3 + ... + r^13/13); the first omitted term is below
-// 2e-8 of the result, so the value is as accurate as the fp32 exp and rcp.
+// softplus(x) = max(x, 0) + ln(1 + w), w = e^{-|x|} in (0, 1], with the
+// hardware exp2 and log2. Forming v = 1 + w rounds w by r = (v - 1) - w
+// (exact in fp32: v - 1 is exact for v in [1, 2], and so is the difference of
+// the two nearby values), and ln(v) = ln(1 + w) + r / v. Subtracting r
+// leaves an error of |r| w / v <= 2^-24 w, i.e. 2^-24 relative to ln(1 + w).
 __device__ __forceinline__ float softplus_f(float x) {
     const float w = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
-    const float r = w * __builtin_amdgcn_rcpf(2.f + w);
-    const float q = r * r;
-    float p = 1.f / 13.f;
-    p = fmaf(p, q, 1.f / 11.f);
-    p = fmaf(p, q, 1.f / 9.f);
-    p = fmaf(p, q, 1.f / 7.f);
-    p = fmaf(p, q, 1.f / 5.f);
-    p = fmaf(p, q, 1.f / 3.f);
-    p = fmaf(p, q, 1.f);
-    return fmaxf(x, 0.f) + 2.f * r * p;
+    const float v = 1.f + w;
+    const float r = (v - 1.f) - w;
+    return fmaf(kLn2, __builtin_amdgcn_logf(v), fmaxf(x, 0.f) - r);
 }
 // silu(z) = z * sigmoid(z) = z / (1 + e^{-z})
 __device__ __forceinline__ float silu_f(float z) {
@@ -258,7 +255,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
-    __shared__ __attribute__((aligned(16))) float tile[2][kSides][2][kRowLanes][kTilePad];
+    // two B/C tile buffers
+    constexpr int kBufFloats = kSides * 2 * kRowLanes * kPairPad;
+    __shared__ __attribute__((aligned(16))) float tile_mem[2 * kBufFloats];
+    float (&tile)[2][kSides][2][kRowLanes][kPairPad] =
+        *reinterpret_cast<float (*)[2][kSides][2][kRowLanes][kPairPad]>(tile_mem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -333,51 +334,139 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         return reinterpret_cast<T*>(yb + (rowoff + static_cast<uint32_t>(p)) * kEs);
     };
 
-    // ---- B/C staging: thread (sn = tid/16, slot = tid%16) copies entry
-    // (state sn, token slot) of every (side, B|C) tile. Rows of states >=
-    // dstate stay zero (written once), so those state lanes never change.
-    // Vim's two sides read the shared B/C at tokens t and L-1-t; each
-    // cross-scan direction reads its own B/C, stored in its scan order.
-    constexpr int kStage = kSides * 2;
-    const int sn = tid >> 4, slot = tid & 15;
-    const bool sn_ok = sn < a.dstate;
+    // ---- B/C staging, one tile per pair of blocks (32 tokens). The tile's
+    // rows are (side, B|C, state); a row's 32 entries are 16-byte chunks (8
+    // bf16 or 4 fp32 entries) that lie contiguously in memory, in token order
+    // or, for a side that reads token L-1-t, in reverse order. Thread tid
+    // loads chunks tid, tid + 256, ... with one 16-byte load each (rows start
+    // at any 2-byte boundary; the target handles unaligned global loads). The
+    // last pair of a sequence that does not fill it is read entry by entry,
+    // clamped. Vim's two sides read the shared B/C at tokens t and L-1-t;
+    // each cross-scan direction reads its own B/C, stored in its scan order.
+    //
+    // The store builds each fp32 tile entry with one byte permute (v_perm)
+    // of two loaded words, the word for token order and the word for reverse
+    // order, so that one selector per chunk does the bf16 widening, the
+    // reversal and, for rows of states >= dstate, the zero fill (those state
+    // lanes then never change). fp32 data that is never reversed (the
+    // cross-scan) is stored as loaded, and the rows of states >= dstate are
+    // zeroed once and never written.
+    constexpr bool kRawStore = sizeof(T) == 4 && MODE == kModeCross4;
+    constexpr int kTpc = 16 / static_cast<int>(sizeof(T));      // entries per chunk
+    constexpr int kCpr = kPairTok / kTpc;                       // chunks per row
+    constexpr int kChunks = kSides * 2 * kRowLanes * kCpr;
+    constexpr int kCpt = (kChunks + kThreads - 1) / kThreads;   // chunks per thread
+    static_assert(kRowLanes * kCpr * 2 % kWaveLanes == 0, "a wave's chunks share one side");
+    // selectors: byte i of the result is byte sel[i] of {S0 (bytes 4-7) : S1
+    // (bytes 0-3)}, 0x0c gives 0. S1 holds the token-order word, S0 the
+    // reverse-order one.
+    constexpr uint32_t kSelZero = 0x0c0c0c0cu;
+    constexpr uint32_t kSelFwdX = sizeof(T) == 2 ? 0x01000c0cu : 0x03020100u;   // S1 low half / word
+    constexpr uint32_t kSelFwdY = sizeof(T) == 2 ? 0x03020c0cu : 0x03020100u;   // S1 high half / word
+    constexpr uint32_t kSelRevX = sizeof(T) == 2 ? 0x07060c0cu : 0x07060504u;   // S0 high half / word
+    constexpr uint32_t kSelRevY = sizeof(T) == 2 ? 0x05040c0cu : 0x07060504u;   // S0 low half / word
     const int64_t bc_dirs = MODE == kModeCross4 ? 4 : (MODE == kModeVim && a.bc_per_dir ? 2 : 1);
-    const uint32_t bc_row = static_cast<uint32_t>((b * bc_dirs * a.dstate + (sn_ok ? sn : 0)) * a.L);
-    const uint32_t bc_dir_stride = static_cast<uint32_t>(a.dstate * a.L);
-    const uint32_t vim_side_stride = MODE == kModeVim && a.bc_per_dir ? bc_dir_stride : 0u;
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
     const char* __restrict__ Cb = static_cast<const char*>(a.C);
-    auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
-        const int t = blk * kBlockTok + slot;
-        const int tc = t < L ? t : L - 1;     // padding slots: any valid entry
+    // chunk j of every thread in a wave lies in rows of one (side, B|C) tile,
+    // so the tensor it reads is uniform per wave: one buffer descriptor over
+    // this batch's B or C
+    const uint32_t bc_batch_el = static_cast<uint32_t>(bc_dirs * a.dstate * a.L);
+    __amdgpu_buffer_rsrc_t csrc[kCpt];
+    uint32_t crow[kCpt];        // row start within the batch (entries)
+    int ccol[kCpt];             // first token of the chunk within the tile
+    bool cin[kCpt];             // the thread has this chunk (uniform per wave)
+    bool crev[kCpt];            // reverse token order (uniform per wave)
+    uint32_t cselx[kCpt], csely[kCpt];
+    bool cok[kCpt];             // the chunk's state row is < dstate
+    int cdst[kCpt];             // tile_mem index of the chunk in buffer 0
 #pragma unroll
-        for (int r = 0; r < kStage; ++r) {
-            uint32_t off;
-            if (MODE == kModeCross4) {
-                off = (bc_row + static_cast<uint32_t>(r >> 1) * bc_dir_stride +
-                       static_cast<uint32_t>(tc)) * kEs;
+    for (int j = 0; j < kCpt; ++j) {
+        const int c0 = tid + j * kThreads;
+        cin[j] = kChunks % kThreads == 0 || __builtin_amdgcn_readfirstlane(c0 < kChunks ? 1 : 0) != 0;
+        const int c = c0 < kChunks ? c0 : 0;
+        const int row = c / kCpr, k = c % kCpr;
+        const int q = row / kRowLanes, srow = row % kRowLanes;
+        const int side = q >> 1;
+        const bool ok_row = srow < a.dstate;
+        const int64_t dsel = MODE == kModeCross4 ? side : (MODE == kModeVim && a.bc_per_dir ? side : 0);
+        const bool isC = __builtin_amdgcn_readfirstlane(q & 1) != 0;
+        csrc[j] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(isC ? Cb : Bb) + static_cast<size_t>(b) * bc_batch_el * kEs, 0,
+            static_cast<int>(bc_batch_el * kEs), 0x00020000);
+        crow[j] = static_cast<uint32_t>((dsel * a.dstate + (ok_row ? srow : 0)) * a.L);
+        ccol[j] = k * kTpc;
+        const bool rv = MODE == kModeVim ? side == 1 : (MODE == kMode1D ? a.reverse != 0 : false);
+        crev[j] = MODE != kModeCross4 && __builtin_amdgcn_readfirstlane(rv ? 1 : 0) != 0;
+        cok[j] = ok_row;
+        cselx[j] = !ok_row ? kSelZero : (rv ? kSelRevX : kSelFwdX);
+        csely[j] = !ok_row ? kSelZero : (rv ? kSelRevY : kSelFwdY);
+        cdst[j] = ((side * 2 + (q & 1)) * kRowLanes + srow) * kPairPad + k * kTpc;
+    }
+    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) {
+        const bool whole = (pair + 1) * kPairTok <= L;      // uniform
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j) {
+            if (!cin[j]) continue;
+            const int t0 = pair * kPairTok + ccol[j];
+            if (whole) {
+                const uint32_t first = crev[j] ? static_cast<uint32_t>(L - kTpc - t0) : static_cast<uint32_t>(t0);
+                raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       csrc[j], static_cast<int>((crow[j] + first) * kEs), 0, 0));
             } else {
-                const bool side_rev = MODE == kModeVim ? (r >> 1) == 1 : rev;
-                off = (bc_row + (side_rev ? vim_side_stride : 0u) +
-                       static_cast<uint32_t>(side_rev ? L - 1 - tc : tc)) * kEs;
+                // entry i of the chunk in memory order holds token t0 + i
+                // (t0 + kTpc - 1 - i when reversed); padding tokens repeat L-1
+                uint32_t e[kTpc];
+#pragma unroll
+                for (int i = 0; i < kTpc; ++i) {
+                    const int t = t0 + (crev[j] ? kTpc - 1 - i : i);
+                    const int tc = t < L ? t : L - 1;
+                    const int off = static_cast<int>((crow[j] + static_cast<uint32_t>(crev[j] ? L - 1 - tc : tc)) * kEs);
+                    e[i] = sizeof(T) == 2 ? __builtin_amdgcn_raw_buffer_load_b16(csrc[j], off, 0, 0)
+                                          : __builtin_amdgcn_raw_buffer_load_b32(csrc[j], off, 0, 0);
+                }
+                uint32_t w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    w[i] = sizeof(T) == 2 ? (e[2 * i] | (e[2 * i + 1] << 16)) : e[i];
+                raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
             }
-            sr[r] = ld_raw(reinterpret_cast<const T*>(((r & 1) ? Cb : Bb) + off), 0);
         }
     };
-    // threads of states >= dstate write their (unused) values into the
-    // padding column 16 of their tile row, so the store needs no branch
-    const int st_col = sn_ok ? slot : kRowLanes;
-    auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) {
+    auto stage_store = [&](int buf, const uint4 (&raw)[kCpt]) {
 #pragma unroll
-        for (int r = 0; r < kStage; ++r)
-            tile[buf][r >> 1][r & 1][sn][st_col] = from_raw<T>(sr[r]);
-    };
-    if (!sn_ok) {
+        for (int j = 0; j < kCpt; ++j) {
+            if (!cin[j]) continue;
+            float4* d4 = reinterpret_cast<float4*>(&tile_mem[cdst[j] + buf * kBufFloats]);
+            if constexpr (kRawStore) {
+                if (cok[j])
+                    d4[0] = make_float4(__uint_as_float(raw[j].x), __uint_as_float(raw[j].y),
+                                        __uint_as_float(raw[j].z), __uint_as_float(raw[j].w));
+                continue;
+            }
+            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+            // tile columns 2d, 2d + 1 of the chunk: token order takes them from
+            // word d (bf16: its low and high halves) or words 2d, 2d + 1
+            // (fp32); reverse order from word 3 - d (high, low) or words
+            // 3 - 2d, 2 - 2d
+            float f[kTpc];
 #pragma unroll
-        for (int r = 0; r < kStage; ++r) {
-            tile[0][r >> 1][r & 1][sn][slot] = 0.f;
-            tile[1][r >> 1][r & 1][sn][slot] = 0.f;
+            for (int d = 0; d < kTpc / 2; ++d) {
+                const uint32_t fx = sizeof(T) == 2 ? w[d] : w[2 * d];
+                const uint32_t fy = sizeof(T) == 2 ? w[d] : w[2 * d + 1];
+                const uint32_t rx = sizeof(T) == 2 ? w[3 - d] : w[3 - 2 * d];
+                const uint32_t ry = sizeof(T) == 2 ? w[3 - d] : w[2 - 2 * d];
+                f[2 * d] = __uint_as_float(__builtin_amdgcn_perm(rx, fx, cselx[j]));
+                f[2 * d + 1] = __uint_as_float(__builtin_amdgcn_perm(ry, fy, csely[j]));
+            }
+#pragma unroll
+            for (int i = 0; i < kTpc / 4; ++i)
+                d4[i] = make_float4(f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]);
         }
+    };
+    if (kRawStore) {
+        for (int i = tid; i < 2 * kBufFloats; i += kThreads)
+            if ((i / kPairPad) % kRowLanes >= a.dstate) tile_mem[i] = 0.f;
     }
 
     // ---- this lane's token of a block (slot n), clamped into the sequence;
@@ -409,11 +498,18 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             k.z = act_at(zb, (MODE != kModeVim || blk >= Fstep) ? p : 0);
     };
 
-    uint32_t sr[kStage];
+    const int npair = (nblk + 1) / 2;
+    uint4 sr[kCpt];
     stage_load(0, sr);
     stage_store(0, sr);
-    Tok tA{}, tB{};
-    tok_load(0, tA);
+    // token data of the next kTokAhead + 1 blocks rotates through four
+    // register sets, so that the loads of three blocks are in flight while
+    // one block is computed
+    static_assert(kTokAhead == 3, "the loop below rotates four token sets");
+    Tok t0{}, t1{}, t2{}, t3{};
+    tok_load(0, t0);
+    tok_load(nblk > 1 ? 1 : 0, t1);
+    tok_load(nblk > 2 ? 2 : 0, t2);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -422,11 +518,14 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     float* ck_row = nullptr;
     if (CKPT)
         ck_row = a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
-    // One block step. `cur` holds this block's token data (loaded one step
-    // earlier), `nxt` receives the next block's; the loop below alternates
-    // the two so that no register of an in-flight load is ever copied.
+    // One block step. `cur` holds this block's token data (loaded three
+    // steps earlier), `nxt` receives block blk + 3's; the loop below rotates
+    // the sets so that no register of an in-flight load is ever copied. The
+    // first block of a pair issues the next pair's B/C loads, the second
+    // stores them to the other tile buffer and ends with the barrier.
     auto step = [&](const int blk, Tok& cur, Tok& nxt) {
-        const int buf = blk & 1;
+        const int buf = (blk >> 1) & 1;
+        const int half = blk & 1;
         const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
         if (CKPT && active) ck_row[blk * kRowLanes + n] = h;
@@ -438,11 +537,13 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         if (MODE != kMode1D)
             part = __hip_atomic_load(part_at(blk > Fstep ? p : 0), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-        // prefetch the next block; on the last step this reloads the last
-        // block (unused), which keeps the loads free of branches
-        const int nb = blk + 1 < nblk ? blk + 1 : blk;
-        stage_load(nb, sr);
-        tok_load(nb, nxt);
+        // prefetch; near the end this reloads the last pair or block
+        // (unused), which keeps the loads free of branches
+        if (half == 0) {
+            const int pair = blk >> 1;
+            stage_load(pair + 1 < npair ? pair + 1 : pair, sr);
+        }
+        tok_load(blk + kTokAhead < nblk ? blk + kTokAhead : nblk - 1, nxt);
 
         // delta and delta*u of this lane's token (zero in padding slots, which
         // then leave the state unchanged: exp(0) = 1 and no input)
@@ -457,8 +558,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const float du = dlt * cu;
 
         const int side = MODE == kMode1D ? 0 : dir;
-        const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][side][0][n][0]);
-        const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][side][1][n][0]);
+        const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][side][0][n][half * kBlockTok]);
+        const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][side][1][n][half * kBlockTok]);
         float Bv[16], Cv[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -520,18 +621,24 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             }
         }
 
-        stage_store(buf ^ 1, sr);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        if (half == 1) {
+            stage_store(buf ^ 1, sr);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        }
     };
 
     int blk = 0;
-    for (; blk + 1 < nblk; blk += 2) {
-        step(blk, tA, tB);
-        step(blk + 1, tB, tA);
+    for (; blk + 3 < nblk; blk += 4) {
+        step(blk, t0, t3);
+        step(blk + 1, t1, t0);
+        step(blk + 2, t2, t1);
+        step(blk + 3, t3, t2);
     }
-    if (blk < nblk) step(blk, tA, tB);
+    if (blk < nblk) step(blk, t0, t3);
+    if (blk + 1 < nblk) step(blk + 1, t1, t0);
+    if (blk + 2 < nblk) step(blk + 2, t2, t1);
 
     if constexpr (MODE == kModeCross4) {
         // every pair sum of the workgroup's channels is stored: y = (row-major
