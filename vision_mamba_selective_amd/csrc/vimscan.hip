@@ -45,8 +45,6 @@ constexpr int kRowLanes = 16;       // one recurrence per DPP row
 constexpr int kBlockTok = 16;       // tokens per block step
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kTilePad = 20;        // LDS row stride (floats) of a 16-token tile
-constexpr int kPairTok = 32;        // tokens per B/C tile of the forward scan (two blocks)
-constexpr int kPairPad = 36;        // its LDS row stride (floats): conflict-free b128 rows
 constexpr int kTokAhead = 3;        // blocks the forward scan's token loads run ahead
 constexpr int kTr = 32;             // grid transpose tile edge
 constexpr int kTrPad = kTr + 1;
@@ -255,7 +253,13 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
-    // two B/C tile buffers
+    // B/C tiles of kPairTok tokens (4 blocks; 2 for the cross-scan, whose
+    // four sides would otherwise exceed the LDS of three workgroups per CU),
+    // rows padded to kPairPad floats, which keeps the b128 row reads of 16
+    // lanes on distinct banks. Two tile buffers.
+    constexpr int kPairTok = MODE == kModeCross4 ? 32 : 64;
+    constexpr int kPairPad = kPairTok + 4;
+    constexpr int kBpt = kPairTok / kBlockTok;              // blocks per tile
     constexpr int kBufFloats = kSides * 2 * kRowLanes * kPairPad;
     __shared__ __attribute__((aligned(16))) float tile_mem[2 * kBufFloats];
     float (&tile)[2][kSides][2][kRowLanes][kPairPad] =
@@ -334,8 +338,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         return reinterpret_cast<T*>(yb + (rowoff + static_cast<uint32_t>(p)) * kEs);
     };
 
-    // ---- B/C staging, one tile per pair of blocks (32 tokens). The tile's
-    // rows are (side, B|C, state); a row's 32 entries are 16-byte chunks (8
+    // ---- B/C staging, one tile per kPairTok tokens. The tile's rows are
+    // (side, B|C, state); a row's entries are 16-byte chunks (8
     // bf16 or 4 fp32 entries) that lie contiguously in memory, in token order
     // or, for a side that reads token L-1-t, in reverse order. Thread tid
     // loads chunks tid, tid + 256, ... with one 16-byte load each (rows start
@@ -498,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             k.z = act_at(zb, (MODE != kModeVim || blk >= Fstep) ? p : 0);
     };
 
-    const int npair = (nblk + 1) / 2;
+    const int npair = (nblk + kBpt - 1) / kBpt;
     uint4 sr[kCpt];
     stage_load(0, sr);
     stage_store(0, sr);
@@ -521,11 +525,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // One block step. `cur` holds this block's token data (loaded three
     // steps earlier), `nxt` receives block blk + 3's; the loop below rotates
     // the sets so that no register of an in-flight load is ever copied. The
-    // first block of a pair issues the next pair's B/C loads, the second
+    // first block of a tile issues the next tile's B/C loads, the last one
     // stores them to the other tile buffer and ends with the barrier.
     auto step = [&](const int blk, Tok& cur, Tok& nxt) {
-        const int buf = (blk >> 1) & 1;
-        const int half = blk & 1;
+        const int buf = (blk / kBpt) & 1;
+        const int half = blk % kBpt;
         const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
         if (CKPT && active) ck_row[blk * kRowLanes + n] = h;
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // prefetch; near the end this reloads the last pair or block
         // (unused), which keeps the loads free of branches
         if (half == 0) {
-            const int pair = blk >> 1;
+            const int pair = blk / kBpt;
             stage_load(pair + 1 < npair ? pair + 1 : pair, sr);
         }
         tok_load(blk + kTokAhead < nblk ? blk + kTokAhead : nblk - 1, nxt);
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             }
         }
 
-        if (half == 1) {
+        if (half == kBpt - 1) {
             stage_store(buf ^ 1, sr);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
             __builtin_amdgcn_s_barrier();
