@@ -253,11 +253,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
     constexpr int kSides = kDirs;              // one B/C tile per direction
-    // B/C tiles of kPairTok tokens (4 blocks; 2 for the cross-scan, whose
-    // four sides would otherwise exceed the LDS of three workgroups per CU),
-    // rows padded to kPairPad floats, which keeps the b128 row reads of 16
-    // lanes on distinct banks. Two tile buffers.
-    constexpr int kPairTok = MODE == kModeCross4 ? 32 : 64;
+    // B/C tiles of kPairTok tokens (two blocks; measured faster than four
+    // for short and long sequences alike), rows padded to kPairPad floats,
+    // which keeps the b128 row reads of 16 lanes on distinct banks. Two tile
+    // buffers.
+    constexpr int kPairTok = 32;
     constexpr int kPairPad = kPairTok + 4;
     constexpr int kBpt = kPairTok / kBlockTok;              // blocks per tile
     constexpr int kBufFloats = kSides * 2 * kRowLanes * kPairPad;
@@ -343,9 +343,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // bf16 or 4 fp32 entries) that lie contiguously in memory, in token order
     // or, for a side that reads token L-1-t, in reverse order. Thread tid
     // loads chunks tid, tid + 256, ... with one 16-byte load each (rows start
-    // at any 2-byte boundary; the target handles unaligned global loads). The
-    // last pair of a sequence that does not fill it is read entry by entry,
-    // clamped. Vim's two sides read the shared B/C at tokens t and L-1-t;
+    // at any 2-byte boundary; the target handles unaligned global loads). A
+    // last tile that the sequence does not fill is read entry by entry,
+    // clamped, once before the loop (nothing else in flight then) and kept
+    // in registers until its turn. Vim's two sides read the shared B/C at tokens t and L-1-t;
     // each cross-scan direction reads its own B/C, stored in its scan order.
     //
     // The store builds each fp32 tile entry with one byte permute (v_perm)
@@ -407,6 +408,37 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         csely[j] = !ok_row ? kSelZero : (rv ? kSelRevY : kSelFwdY);
         cdst[j] = ((side * 2 + (q & 1)) * kRowLanes + srow) * kPairPad + k * kTpc;
     }
+    const int ntile = (L + kPairTok - 1) / kPairTok;
+    const bool tail_part = ntile * kPairTok > L;                // uniform
+    uint4 tail_raw[kCpt];
+    if (tail_part) {
+        const int pair = ntile - 1;
+#pragma unroll
+        for (int j = 0; j < kCpt; ++j) {
+            if (!cin[j]) continue;
+            const int t0 = pair * kPairTok + ccol[j];
+            // entry i of the chunk in memory order holds token t0 + i
+            // (t0 + kTpc - 1 - i when reversed); padding tokens repeat L-1
+            uint32_t e[kTpc];
+#pragma unroll
+            for (int i = 0; i < kTpc; ++i) {
+                const int t = t0 + (crev[j] ? kTpc - 1 - i : i);
+                const int tc = t < L ? t : L - 1;
+                const int off = static_cast<int>((crow[j] + static_cast<uint32_t>(crev[j] ? L - 1 - tc : tc)) * kEs);
+                e[i] = sizeof(T) == 2 ? __builtin_amdgcn_raw_buffer_load_b16(csrc[j], off, 0, 0)
+                                      : __builtin_amdgcn_raw_buffer_load_b32(csrc[j], off, 0, 0);
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                w[i] = sizeof(T) == 2 ? (e[2 * i] | (e[2 * i + 1] << 16)) : e[i];
+                // materialise here: packing at the use inside the loop would
+                // have to wait for every load then in flight
+                asm volatile("" : "+v"(w[i]));
+            }
+            tail_raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
     auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) {
         const bool whole = (pair + 1) * kPairTok <= L;      // uniform
 #pragma unroll
@@ -418,22 +450,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
                 raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                        csrc[j], static_cast<int>((crow[j] + first) * kEs), 0, 0));
             } else {
-                // entry i of the chunk in memory order holds token t0 + i
-                // (t0 + kTpc - 1 - i when reversed); padding tokens repeat L-1
-                uint32_t e[kTpc];
-#pragma unroll
-                for (int i = 0; i < kTpc; ++i) {
-                    const int t = t0 + (crev[j] ? kTpc - 1 - i : i);
-                    const int tc = t < L ? t : L - 1;
-                    const int off = static_cast<int>((crow[j] + static_cast<uint32_t>(crev[j] ? L - 1 - tc : tc)) * kEs);
-                    e[i] = sizeof(T) == 2 ? __builtin_amdgcn_raw_buffer_load_b16(csrc[j], off, 0, 0)
-                                          : __builtin_amdgcn_raw_buffer_load_b32(csrc[j], off, 0, 0);
-                }
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = sizeof(T) == 2 ? (e[2 * i] | (e[2 * i + 1] << 16)) : e[i];
-                raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
+                raw[j] = tail_raw[j];
             }
         }
     };
@@ -484,7 +501,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // ---- this lane's token of a block; unconditional loads on a valid
     // index so that they can all be in flight together.
     const int Fstep = MODE != kMode1D ? (L - 1) / (2 * kBlockTok) : -1;
-    struct Tok { uint32_t u, dl, z, ul, ur; int p; };
+    // raw entries at their own width: a bf16 entry held zero-extended would
+    // be re-masked where the loop carries it, which waits for its load
+    using Raw = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
+    struct Tok { Raw u, dl, z, ul, ur; int p; };
     auto tok_load = [&](int blk, Tok& k) {
         const int p = tok_pos(blk);
         k.p = p;
@@ -506,14 +526,16 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     uint4 sr[kCpt];
     stage_load(0, sr);
     stage_store(0, sr);
-    // token data of the next kTokAhead + 1 blocks rotates through four
-    // register sets, so that the loads of three blocks are in flight while
-    // one block is computed
-    static_assert(kTokAhead == 3, "the loop below rotates four token sets");
-    Tok t0{}, t1{}, t2{}, t3{};
-    tok_load(0, t0);
-    tok_load(nblk > 1 ? 1 : 0, t1);
-    tok_load(nblk > 2 ? 2 : 0, t2);
+    // token data rotates through kTokAhead + 1 register sets, so that the
+    // loads of kTokAhead blocks are in flight while one block is computed
+    // (deeper prefetch measured no faster)
+    constexpr int kRing = kTokAhead + 1;
+    static_assert(kRing % kBpt == 0, "a loop trip covers whole tiles");
+    Tok tk[kRing];
+    Unroll<kTokAhead>::run([&](auto ic) {
+        constexpr int k = decltype(ic)::value;
+        tok_load(k < nblk ? k : nblk - 1, tk[k]);
+    });
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -522,9 +544,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     float* ck_row = nullptr;
     if (CKPT)
         ck_row = a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
-    // One block step. `cur` holds this block's token data (loaded three
-    // steps earlier), `nxt` receives block blk + 3's; the loop below rotates
-    // the sets so that no register of an in-flight load is ever copied. The
+    // One block step. `cur` holds this block's token data (loaded kTokAhead
+    // steps earlier), `nxt` receives block blk + kTokAhead's; the loop below
+    // rotates the sets so that no register of an in-flight load is ever
+    // copied. The
     // first block of a tile issues the next tile's B/C loads, the last one
     // stores them to the other tile buffer and ends with the barrier.
     auto step = [&](const int blk, Tok& cur, Tok& nxt) {
@@ -633,16 +656,18 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
     };
 
+    // slot k of the ring holds block blk + k at the top of every trip
     int blk = 0;
-    for (; blk + 3 < nblk; blk += 4) {
-        step(blk, t0, t3);
-        step(blk + 1, t1, t0);
-        step(blk + 2, t2, t1);
-        step(blk + 3, t3, t2);
+    for (; blk + kTokAhead < nblk; blk += kRing) {
+        Unroll<kRing>::run([&](auto ic) {
+            constexpr int k = decltype(ic)::value;
+            step(blk + k, tk[k], tk[(k + kTokAhead) % kRing]);
+        });
     }
-    if (blk < nblk) step(blk, t0, t3);
-    if (blk + 1 < nblk) step(blk + 1, t1, t0);
-    if (blk + 2 < nblk) step(blk + 2, t2, t1);
+    Unroll<kTokAhead>::run([&](auto ic) {
+        constexpr int k = decltype(ic)::value;
+        if (blk + k < nblk) step(blk + k, tk[k], tk[(k + kTokAhead) % kRing]);
+    });
 
     if constexpr (MODE == kModeCross4) {
         // every pair sum of the workgroup's channels is stored: y = (row-major
