@@ -84,6 +84,11 @@ struct ScanArgs {
     int nblk;           // ceil(L / 16)
 };
 
+// The kernels' per-block steps are lambdas over register arrays (token
+// sets, tiles' raw words); one left out of line would put those arrays in
+// scratch memory.
+#define VS_INLINE __attribute__((always_inline))
+
 // ---------------------------------------------------------------- dtype I/O
 __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ld(const uint16_t* p, int64_t i) {
@@ -439,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             tail_raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
         }
     }
-    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) {
+    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) VS_INLINE {
         const bool whole = (pair + 1) * kPairTok <= L;      // uniform
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
@@ -454,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             }
         }
     };
-    auto stage_store = [&](int buf, const uint4 (&raw)[kCpt]) {
+    auto stage_store = [&](int buf, const uint4 (&raw)[kCpt]) VS_INLINE {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
             if (!cin[j]) continue;
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // be re-masked where the loop carries it, which waits for its load
     using Raw = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
     struct Tok { Raw u, dl, z, ul, ur; int p; };
-    auto tok_load = [&](int blk, Tok& k) {
+    auto tok_load = [&](int blk, Tok& k) VS_INLINE {
         const int p = tok_pos(blk);
         k.p = p;
         k.u = act_row(ub, u_row, p);
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // copied. The
     // first block of a tile issues the next tile's B/C loads, the last one
     // stores them to the other tile buffer and ends with the barrier.
-    auto step = [&](const int blk, Tok& cur, Tok& nxt) {
+    auto step = [&](const int blk, Tok& cur, Tok& nxt) VS_INLINE {
         const int buf = (blk / kBpt) & 1;
         const int half = blk % kBpt;
         const int p = cur.p;
@@ -841,7 +846,7 @@ void rowgrad_kernel(const GradArgs a) {
     const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
     const char* __restrict__ Cb = static_cast<const char*>(a.C);
-    auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) {
+    auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) VS_INLINE {
         const int t = blk * kBlockTok + slot;
         const int tc = t < L ? t : L - 1;
 #pragma unroll
@@ -851,7 +856,7 @@ void rowgrad_kernel(const GradArgs a) {
         }
     };
     const int st_col = sn_ok ? slot : kRowLanes;
-    auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) {
+    auto stage_store = [&](int buf, const uint32_t (&sr)[kStage]) VS_INLINE {
         if (stager) {
 #pragma unroll
             for (int r = 0; r < kStage; ++r)
@@ -881,7 +886,7 @@ void rowgrad_kernel(const GradArgs a) {
     };
     const int Fstep = (L - 1) / (2 * kBlockTok);
     struct Tok { uint32_t u, dl, z, g; float s, h0; int p; };
-    auto tok_load = [&](int blk, Tok& k) {
+    auto tok_load = [&](int blk, Tok& k) VS_INLINE {
         const int p = tok_pos(blk);
         k.p = p;
         const float h0 = ck_row[blk * kRowLanes + n];            // state at the block's start
@@ -937,7 +942,7 @@ void rowgrad_kernel(const GradArgs a) {
     // (partial added, du and ddelta written); block F mixes both.
     constexpr int kFirst = 0, kMixed = 1, kSecond = 2;
     float lam = 0.f, e_carry = 0.f, dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
-    auto step = [&](auto phase, const int blk, Tok& cur, Tok& nxt) {
+    auto step = [&](auto phase, const int blk, Tok& cur, Tok& nxt) VS_INLINE {
         constexpr int PH = decltype(phase)::value;
         const int buf = blk & 1;
         const int p = cur.p;
