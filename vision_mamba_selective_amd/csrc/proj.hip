@@ -12,16 +12,20 @@
 //
 // proj_gemm_kernel computes one batch row's Out[M][L] = W[M][K] X[K][L] in
 // BM x BN tiles with v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
-// accumulation). Per 32-deep slice of K, W's rows are copied to LDS as they
-// are (k contiguous) and X's columns are gathered one per thread so that LDS
-// holds them k-contiguous too: the MFMA takes 8 consecutive k of one row
-// (A) and of one column (B) per lane. The next slice is loaded into
-// registers while the matrix cores work on the current one. Four waves in a
-// 2 x 2 grid each own (BM/2) x (BN/2) of the tile. out_proj's epilogue stages
-// the tile through LDS, so that the residual is read and the result written
-// in whole rows. Measured at Vim-S 1024^2 (768 -> 768, 8 x 4,097 tokens):
-// 128 x 64 tiles beat 128 x 128 and 64 x 128 (more workgroups per CU hide
-// more of the global-load latency, which bounds this kernel).
+// accumulation), which takes 8 consecutive k of one row of W (A) and of one
+// column of X (B) per lane. Per 64-deep slice of K, W's rows are copied to
+// LDS as they are (k contiguous), and X's rows too (token contiguous), 16
+// bytes per load: X rows start at any 2-byte boundary (L is odd), which the
+// target's unaligned global access handles. The B fragments come out of LDS
+// with ds_read_b64_tr_b16, which transposes 4 x 16 blocks of b16 within each
+// 16-lane group: a lane reading 4 tokens of one k row contributes element i
+// to lane i of its group, so every lane receives 4 consecutive k of its own
+// token. The next slice is loaded into registers while the matrix cores
+// work on the current one (two slices ahead measured slower: the second
+// register set costs more occupancy than the latency it hides). Four waves in a 2 x 2 grid each own (BM/2) x
+// (BN/2) of the tile. out_proj's epilogue stages the tile through LDS, so
+// that the residual is read and the result written in whole rows. The last
+// tile of a row, which passes the sequence end, reads X entry by entry.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -37,6 +41,10 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr int kThreads = 256;
 constexpr int kBK = 64;                 // K per LDS slice
 constexpr int kRow = kBK + 8;           // LDS row: 64 bf16 + 8 padding (144 bytes)
+constexpr int kXPad = 16;               // X slice rows: BN + 16 bf16, 160 bytes for BN = 64,
+                                        // which puts the 4 rows x 2 token halves that a
+                                        // transposing read touches per 32 lanes on
+                                        // distinct banks
 
 enum { kEpiOut = 0, kEpiXproj = 1 };
 
@@ -57,14 +65,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));   // round to nearest even
 }
 
+typedef __attribute__((ext_vector_type(4))) short v4s;
+
 template <int BM, int BN, int EPI, bool WVEC>
 __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     static_assert(BM % 64 == 0 && BN % 64 == 0, "2 x 2 waves of 32 x 32 MFMA tiles");
     constexpr int TM = BM / 64, TN = BN / 64;
-    // X slice: each column of BN is gathered by kThreads / BN threads, KPT k each
-    constexpr int kColThreads = kThreads / BN;
-    constexpr int KPT = kBK / kColThreads;
-    static_assert(KPT % 8 == 0, "whole 16-byte LDS rows");
+    // X slice: kBK rows of BN tokens, 16-byte chunks of 8 tokens
+    constexpr int kXRow = BN + kXPad;
+    constexpr int kXChunks = kBK * BN / 8;
+    static_assert(kXChunks % kThreads == 0, "whole chunks per thread");
+    constexpr int kXcpt = kXChunks / kThreads;
     // W slice: 16-byte chunks (WVEC) or single elements
     constexpr int kChunks = BM * kBK / 8;
     constexpr int kChunkPT = (kChunks + kThreads - 1) / kThreads;
@@ -74,11 +85,12 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     // tile (bf16, rows of BN + 8), staged so that residual reads and result
     // writes move whole rows of the tile
     constexpr int kOutRow = BN + 8;
-    constexpr int kSmem = (BM + BN) * kRow > BM * kOutRow ? (BM + BN) * kRow : BM * kOutRow;
+    constexpr int kOps = BM * kRow + kBK * kXRow;
+    constexpr int kSmem = kOps > BM * kOutRow ? kOps : BM * kOutRow;
     __shared__ __attribute__((aligned(16))) uint16_t smem[kSmem];
     __shared__ float sBias[BM];
     uint16_t (*sA)[kRow] = reinterpret_cast<uint16_t (*)[kRow]>(smem);
-    uint16_t (*sB)[kRow] = reinterpret_cast<uint16_t (*)[kRow]>(smem + BM * kRow);
+    uint16_t (*sX)[kXRow] = reinterpret_cast<uint16_t (*)[kXRow]>(smem + BM * kRow);
     uint16_t (*sT)[kOutRow] = reinterpret_cast<uint16_t (*)[kOutRow]>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -104,13 +116,14 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     const int M = a.M, K = a.K, L = a.L;
     const uint16_t* __restrict__ Xb = a.X + b * static_cast<int64_t>(K) * L;
 
-    // this thread's X column (clamped: columns past L feed only masked outputs)
-    const int xn = tid % BN, xk = (tid / BN) * KPT;
-    const int64_t xcol = n0 + xn < L ? n0 + xn : L - 1;
+    // the tile's tokens all lie inside the sequence (uniform per workgroup);
+    // else X is read entry by entry, clamped (tokens past L feed only masked
+    // outputs)
+    const bool xwhole = n0 + BN <= L;
 
     uint4 wreg[WVEC ? kChunkPT : 1];
     uint16_t wel[WVEC ? 1 : kElemPT];
-    uint16_t xreg[KPT];
+    uint4 xreg[kXcpt];
     auto load_slice = [&](int k0) {
         if (WVEC) {
 #pragma unroll
@@ -131,10 +144,22 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
             }
         }
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            const int k = k0 + xk + j;
+        for (int i = 0; i < kXcpt; ++i) {
+            const int c = tid + i * kThreads;
+            const int r = c / (BN / 8), nc = (c % (BN / 8)) * 8;
             // rows past K: any finite value (W is zero there)
-            xreg[j] = Xb[static_cast<int64_t>(k < K ? k : K - 1) * L + xcol];
+            const uint16_t* src = Xb + static_cast<int64_t>(k0 + r < K ? k0 + r : K - 1) * L;
+            if (xwhole) {
+                __builtin_memcpy(&xreg[i], src + n0 + nc, 16);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t0 = n0 + nc + 2 * e, t1 = t0 + 1;
+                    w[e] = uint32_t(src[t0 < L ? t0 : L - 1]) | (uint32_t(src[t1 < L ? t1 : L - 1]) << 16);
+                }
+                xreg[i] = make_uint4(w[0], w[1], w[2], w[3]);
+            }
         }
     };
     auto store_slice = [&]() {
@@ -153,13 +178,9 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
             }
         }
 #pragma unroll
-        for (int q = 0; q < KPT / 8; ++q) {
-            uint4 v;
-            v.x = xreg[8 * q] | (uint32_t(xreg[8 * q + 1]) << 16);
-            v.y = xreg[8 * q + 2] | (uint32_t(xreg[8 * q + 3]) << 16);
-            v.z = xreg[8 * q + 4] | (uint32_t(xreg[8 * q + 5]) << 16);
-            v.w = xreg[8 * q + 6] | (uint32_t(xreg[8 * q + 7]) << 16);
-            *reinterpret_cast<uint4*>(&sB[xn][xk + 8 * q]) = v;
+        for (int i = 0; i < kXcpt; ++i) {
+            const int c = tid + i * kThreads;
+            *reinterpret_cast<uint4*>(&sX[c / (BN / 8)][(c % (BN / 8)) * 8]) = xreg[i];
         }
     };
 
@@ -174,6 +195,11 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     if (EPI == kEpiOut && tid < BM)
         sBias[tid] = (a.bias && m0 + tid < M) ? a.bias[m0 + tid] : 0.f;
     const int fr = lane & 31, fk = 8 * (lane >> 5);     // fragment row / column, k offset
+    // transposing reads of X: lane 4e + q of a 16-lane group reads 4 tokens
+    // (4q ..) of k row e of its group's 4 x 16 block; group g covers k rows
+    // 8 (g / 2) .. and tokens 16 (g % 2) ..
+    const int tg = lane >> 4, tp = lane & 15;
+    const int tk = 8 * (tg >> 1) + (tp >> 2), tn = 16 * (tg & 1) + 4 * (tp & 3);
     load_slice(0);
     for (int k0 = 0; k0 < K; k0 += kBK) {
         store_slice();
@@ -186,8 +212,16 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
             for (int i = 0; i < TM; ++i)
                 fa[i] = *reinterpret_cast<const bf16x8*>(&sA[wm * (BM / 2) + i * 32 + fr][ks + fk]);
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8*>(&sB[wn * (BN / 2) + j * 32 + fr][ks + fk]);
+            for (int j = 0; j < TN; ++j) {
+                const int nb = wn * (BN / 2) + j * 32 + tn;
+                const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s*)(&sX[ks + tk][nb]));
+                const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) v4s*)(&sX[ks + tk + 4][nb]));
+                const __attribute__((ext_vector_type(8))) short v8 = {lo[0], lo[1], lo[2], lo[3],
+                                                                     hi[0], hi[1], hi[2], hi[3]};
+                fb[j] = __builtin_bit_cast(bf16x8, v8);
+            }
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -199,18 +233,32 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
 
     // accumulator r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
     if (EPI == kEpiOut) {
-        // 1. the residual tile into LDS, whole rows per instruction (rows and
+        // 1. the residual tile into LDS, 16 bytes (8 tokens of a row) per
+        //    load; the last tile of a row entry by entry, clamped (rows and
         //    columns past the matrix: any valid element, never stored)
-        constexpr int kRowsPT = BM * BN / kThreads;         // rows per thread
-        const int tn = tid % BN, tr0 = tid / BN;
-        constexpr int kRowStep = kThreads / BN;
-        const int64_t ncl = n0 + tn < L ? n0 + tn : L - 1;
+        constexpr int kOutChunks = BM * BN / 8;
+        static_assert(kOutChunks % kThreads == 0, "whole chunks per thread");
+        constexpr int kOcpt = kOutChunks / kThreads;
         if (a.res) {
-#pragma unroll 16
-            for (int q = 0; q < kRowsPT; ++q) {
-                const int row = tr0 + q * kRowStep;
+#pragma unroll
+            for (int q = 0; q < kOcpt; ++q) {
+                const int c = tid + q * kThreads;
+                const int row = c / (BN / 8), nc = (c % (BN / 8)) * 8;
                 const int64_t mcl = m0 + row < M ? m0 + row : M - 1;
-                sT[row][tn] = a.res[(b * M + mcl) * static_cast<int64_t>(L) + ncl];
+                const uint16_t* src = a.res + (b * M + mcl) * static_cast<int64_t>(L);
+                uint4 v;
+                if (xwhole) {
+                    __builtin_memcpy(&v, src + n0 + nc, 16);
+                } else {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t0 = n0 + nc + 2 * e, t1 = t0 + 1;
+                        w[e] = uint32_t(src[t0 < L ? t0 : L - 1]) | (uint32_t(src[t1 < L ? t1 : L - 1]) << 16);
+                    }
+                    v = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+                *reinterpret_cast<uint4*>(&sT[row][nc]) = v;
             }
         }
         __syncthreads();
@@ -229,13 +277,22 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
                 }
             }
         __syncthreads();
-        // 3. whole rows out
-        if (n0 + tn < L) {
-#pragma unroll 16
-            for (int q = 0; q < kRowsPT; ++q) {
-                const int row = tr0 + q * kRowStep;
-                if (m0 + row < M)
-                    a.out[(b * M + m0 + row) * static_cast<int64_t>(L) + n0 + tn] = sT[row][tn];
+        // 3. the tile out, 16 bytes per store (the last tile of a row entry
+        //    by entry)
+#pragma unroll
+        for (int q = 0; q < kOcpt; ++q) {
+            const int c = tid + q * kThreads;
+            const int row = c / (BN / 8), nc = (c % (BN / 8)) * 8;
+            if (m0 + row >= M) continue;
+            uint16_t* dst = a.out + (b * M + m0 + row) * static_cast<int64_t>(L) + n0 + nc;
+            const uint4 v = *reinterpret_cast<const uint4*>(&sT[row][nc]);
+            if (xwhole) {
+                __builtin_memcpy(dst, &v, 16);
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (n0 + nc + e < L) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
             }
         }
     } else {
