@@ -791,8 +791,10 @@ void rowgrad_kernel(const GradArgs a) {
     constexpr int kWaves = CH / 2;
     static_assert(CH % 4 == 0, "whole waves, and at least the 256 staging threads");
     __shared__ __attribute__((aligned(16))) float tile[2][2][2][kRowLanes][kTilePad];
-    // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap
-    __shared__ __attribute__((aligned(16))) float red[kWaves][kWaveLanes][kTilePad];
+    // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap;
+    // two buffers, so that a block's sums are reduced while the waves go on
+    // to the next block (one barrier per block)
+    __shared__ __attribute__((aligned(16))) float red[2][kWaves][kWaveLanes][kTilePad];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -877,7 +879,8 @@ void rowgrad_kernel(const GradArgs a) {
     // the first 256 threads store the chunk (a float4 each); the others get
     // an out-of-range offset
     const int chunk_off = stager ? tid * 16 : kBcChunk * 4;
-    float4* const red_lane = reinterpret_cast<float4*>(&red[tid >> 6][lane][0]);
+    float4* const red_lane0 = reinterpret_cast<float4*>(&red[0][tid >> 6][lane][0]);
+    float4* const red_lane1 = reinterpret_cast<float4*>(&red[1][tid >> 6][lane][0]);
 
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
@@ -1051,20 +1054,26 @@ void rowgrad_kernel(const GradArgs a) {
             }
         }
 
-        // sum the four waves' dB/dC in LDS into the block's chunk, and
-        // stage the next block's B/C
+        // stage the next block's B/C (that buffer was last read before the
+        // previous barrier), write this block's dB/dC sums, and after the
+        // barrier sum the waves' sums into the block's chunk. The next block
+        // writes the other sum buffer, whose reduction finished before this
+        // barrier, so one barrier per block covers both.
+        stage_store(buf ^ 1, sr);
+        float4* const red_lane = (blk & 1) ? red_lane1 : red_lane0;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             red_lane[q] = make_float4(sbc[4 * q], sbc[4 * q + 1], sbc[4 * q + 2], sbc[4 * q + 3]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        {
+        if (stager) {
+            const int rb = blk & 1;
             const int rl = (tid >> 2) & (kWaveLanes - 1), i0 = (tid & 3) * 4;
-            float4 acc = *reinterpret_cast<const float4*>(&red[0][rl][i0]);
+            float4 acc = *reinterpret_cast<const float4*>(&red[rb][0][rl][i0]);
 #pragma unroll
             for (int w = 1; w < kWaves; ++w) {
-                const float4 v = *reinterpret_cast<const float4*>(&red[w][rl][i0]);
+                const float4 v = *reinterpret_cast<const float4*>(&red[rb][w][rl][i0]);
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             const auto rc = __builtin_amdgcn_make_buffer_rsrc(bc_chunks + static_cast<size_t>(blk) * kBcChunk,
@@ -1072,10 +1081,6 @@ void rowgrad_kernel(const GradArgs a) {
             __builtin_amdgcn_raw_buffer_store_b128(
                 __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, acc), rc, chunk_off, 0, 0);
         }
-        stage_store(buf ^ 1, sr);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     };
 
     // Each phase is its own loop with the same memory operations on every
