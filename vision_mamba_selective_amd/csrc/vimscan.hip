@@ -984,6 +984,11 @@ void rowgrad_kernel(const GradArgs a) {
             }
         }
         gs = ok ? gs : 0.f;
+        // second copies of the broadcast sources, opaque to the compiler, so
+        // that each broadcast has one use and folds into it as a DPP operand
+        // (one shared broadcast would cost a separate v_mov_b32_dpp)
+        float dlt2 = dlt, du2 = du_, gs2 = gs;
+        asm volatile("" : "+v"(dlt2), "+v"(du2), "+v"(gs2));
 
         const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][dir][0][n][0]);
         const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][dir][1][n][0]);
@@ -1011,14 +1016,13 @@ void rowgrad_kernel(const GradArgs a) {
         Unroll<16>::run([&](auto ic) {
             constexpr int i = 15 - decltype(ic)::value;
             const float e_next = i < 15 ? es[i < 15 ? i + 1 : 15] : e_carry;
-            const float g_i = row_bcast<i>(gs);
-            lam = fmaf(e_next, lam, g_i * Cv[i]);
+            lam = fmaf(e_next, lam, row_bcast<i>(gs) * Cv[i]);
             const float hprev = i > 0 ? hs[i > 0 ? i - 1 : 0] : h_in;
             const float q = lam * hprev * es[i];
-            dA_acc = fmaf(q, row_bcast<i>(dlt), dA_acc);
+            dA_acc = fmaf(row_bcast<i>(dlt2), q, dA_acc);
             wv[i] = lam * Bv[i];
             vv[i] = q * An;
-            sbc[i] = swap32_sum(lam * row_bcast<i>(du_), g_i * hs[i]);
+            sbc[i] = swap32_sum(row_bcast<i>(du2) * lam, row_bcast<i>(gs2) * hs[i]);
         });
         e_carry = es[0];
         const float Rw = row_transpose_sum(wv, lane);
