@@ -682,47 +682,76 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        float (*tr)[kTrPad] = reinterpret_cast<float (*)[kTrPad]>(&tile[0][0][0][0][0]);
+        // The tiles of all the workgroup's channels form one list, taken
+        // kGroup at a time: the loads of a whole group are issued together,
+        // then its column-major tiles are transposed through LDS, with two
+        // barriers per group (one tile at a time left this phase waiting on
+        // load latency: about 50 us per workgroup at 64 x 64).
+        constexpr int kGroup = 8;
+        static_assert(kGroup * kTr * kTrPad <= 2 * kBufFloats, "the transposition tiles fit the tile buffers");
+        constexpr int kRpt = kTr * kTr / kThreads;           // tile rows per thread
+        static_assert(kRpt * kThreads == kTr * kTr, "whole tile rows per thread");
+        float (*tr)[kTr][kTrPad] = reinterpret_cast<float (*)[kTr][kTrPad]>(&tile_mem[0]);
         const char* __restrict__ p0 = reinterpret_cast<const char*>(a.partial);
         const char* __restrict__ p1 = reinterpret_cast<const char*>(a.partial2);
         const int H = a.H, Wd = a.W;
         const int tx = tid & (kTr - 1), ty = tid / kTr;
         const int tiles_w = (Wd + kTr - 1) / kTr, ntiles = tiles_w * ((H + kTr - 1) / kTr);
         const int64_t dfirst = static_cast<int64_t>(cg) * kChPerWg;
-        for (int c = 0; c < kChPerWg; ++c) {
-            if (dfirst + c >= a.dim) break;
-            const uint32_t off = static_cast<uint32_t>((b * a.dim + dfirst + c) * a.L);
-            for (int tile_id = 0; tile_id < ntiles; ++tile_id) {
+        const int nch = static_cast<int>(a.dim - dfirst < kChPerWg ? a.dim - dfirst : kChPerWg);
+        const int items = nch * ntiles;
+        auto ld_part = [&](const char* base, uint32_t o) {
+            return __hip_atomic_load(reinterpret_cast<const float*>(base + o * 4u), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        };
+        for (int g0 = 0; g0 < items; g0 += kGroup) {
+            float vc[kGroup][kRpt], vr[kGroup][kRpt], zg[kGroup][kRpt];
+            uint32_t orow[kGroup][kRpt];
+            bool okrow[kGroup][kRpt];
+            // 1. every load of the group: column-major sums of column j0 + r,
+            //    row i0 + tx (to transpose), and the row-major sums (and z)
+            //    of row i0 + r, column j0 + tx
+#pragma unroll
+            for (int g = 0; g < kGroup; ++g) {
+                const int it = g0 + g;
+                const bool have = it < items;                     // uniform
+                const int c = have ? it / ntiles : 0, tile_id = have ? it % ntiles : 0;
+                const uint32_t off = static_cast<uint32_t>((b * a.dim + dfirst + c) * a.L);
                 const int i0 = (tile_id / tiles_w) * kTr, j0 = (tile_id % tiles_w) * kTr;
 #pragma unroll
-                for (int r = ty; r < kTr; r += kThreads / kTr) {
-                    const int i = i0 + tx, j = j0 + r;        // column j, row i
-                    if (i < H && j < Wd) {
-                        const uint32_t o = off + static_cast<uint32_t>(j * H + i);
-                        tr[r][tx] = __hip_atomic_load(reinterpret_cast<const float*>(p1 + o * 4u),
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                for (int q = 0; q < kRpt; ++q) {
+                    const int r = ty + q * (kThreads / kTr);
+                    const bool okc = have && i0 + tx < H && j0 + r < Wd;
+                    vc[g][q] = okc ? ld_part(p1, off + static_cast<uint32_t>((j0 + r) * H + i0 + tx)) : 0.f;
+                    okrow[g][q] = have && i0 + r < H && j0 + tx < Wd;
+                    orow[g][q] = off + static_cast<uint32_t>((i0 + r) * Wd + j0 + tx);
+                    vr[g][q] = okrow[g][q] ? ld_part(p0, orow[g][q]) : 0.f;
+                    zg[g][q] = 1.f;
+                    if (GATE && okrow[g][q])
+                        zg[g][q] = from_raw<T>(ld_raw(reinterpret_cast<const T*>(zb + orow[g][q] * kEs), 0));
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-#pragma unroll
-                for (int r = ty; r < kTr; r += kThreads / kTr) {
-                    const int i = i0 + r, j = j0 + tx;        // row i, column j
-                    if (i < H && j < Wd) {
-                        const uint32_t o = off + static_cast<uint32_t>(i * Wd + j);
-                        float v = __hip_atomic_load(reinterpret_cast<const float*>(p0 + o * 4u),
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) +
-                                  tr[tx][r];
-                        if (GATE)
-                            v *= silu_f(from_raw<T>(ld_raw(reinterpret_cast<const T*>(zb + o * kEs), 0)));
-                        st(reinterpret_cast<T*>(yb + o * kEs), 0, v);
-                    }
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-                __builtin_amdgcn_s_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             }
+            // 2. the column-major tiles into LDS, transposed on the way out
+#pragma unroll
+            for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+                for (int q = 0; q < kRpt; ++q) tr[g][ty + q * (kThreads / kTr)][tx] = vc[g][q];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            // 3. y = (row-major pair + column-major pair) * gate
+#pragma unroll
+            for (int g = 0; g < kGroup; ++g)
+#pragma unroll
+                for (int q = 0; q < kRpt; ++q) {
+                    if (!okrow[g][q]) continue;
+                    float v = vr[g][q] + tr[g][tx][ty + q * (kThreads / kTr)];
+                    if (GATE) v *= silu_f(zg[g][q]);
+                    st(reinterpret_cast<T*>(yb + orow[g][q] * kEs), 0, v);
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         }
     }
 }
