@@ -320,16 +320,47 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     }
 }
 
-// dt_proj without its bias: delta[b][d][t] = w[d] dt[b][t], in bf16.
+// dt_proj without its bias: delta[b][d][t] = w[d] dt[b][t], in bf16. A thread
+// takes kDtTok consecutive tokens of kDtCh channels: it reads their dt once
+// and writes 16 bytes per channel (rows start at any 2-byte boundary, which
+// the target's unaligned global access handles; the last chunk of a row,
+// past the sequence end, is written entry by entry).
+constexpr int kDtTok = 8, kDtCh = 8;
 __global__ __launch_bounds__(kThreads) void dt_proj_kernel(const float* __restrict__ dt,
                                                            const float* __restrict__ w,
                                                            uint16_t* __restrict__ delta, int dim,
                                                            int L) {
-    const int t = blockIdx.x * kThreads + threadIdx.x;
-    if (t >= L) return;
-    const int d = blockIdx.y;
+    const int t0 = (blockIdx.x * kThreads + threadIdx.x) * kDtTok;
+    if (t0 >= L) return;
     const int64_t b = blockIdx.z;
-    delta[(b * dim + d) * static_cast<int64_t>(L) + t] = f32_to_bf16(w[d] * dt[b * L + t]);
+    const int d0 = blockIdx.y * kDtCh;
+    const float* src = dt + b * L + t0;
+    const bool whole = t0 + kDtTok <= L;
+    float v[kDtTok];
+    if (whole) {
+        __builtin_memcpy(v, src, sizeof(v));
+    } else {
+#pragma unroll
+        for (int i = 0; i < kDtTok; ++i) v[i] = t0 + i < L ? src[i] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kDtCh; ++c) {
+        const int d = d0 + c;
+        if (d >= dim) break;
+        const float wd = w[d];
+        uint32_t pk[kDtTok / 2];
+#pragma unroll
+        for (int i = 0; i < kDtTok / 2; ++i)
+            pk[i] = uint32_t(f32_to_bf16(wd * v[2 * i])) | (uint32_t(f32_to_bf16(wd * v[2 * i + 1])) << 16);
+        uint16_t* dst = delta + (b * dim + d) * static_cast<int64_t>(L) + t0;
+        if (whole) {
+            __builtin_memcpy(dst, pk, sizeof(pk));
+        } else {
+#pragma unroll
+            for (int e = 0; e < kDtTok; ++e)
+                if (t0 + e < L) dst[e] = static_cast<uint16_t>(pk[e >> 1] >> (16 * (e & 1)));
+        }
+    }
 }
 
 bool overlap(const void* p, size_t np, const void* q, size_t nq) {
@@ -421,8 +452,9 @@ int vim_dt_proj(int64_t batch, int64_t dim, int64_t seqlen, int dtype, const flo
     if (overlap(delta, nd, dt, static_cast<size_t>(batch * seqlen) * 4) ||
         overlap(delta, nd, w, static_cast<size_t>(dim) * 4))
         return vs_internal_fail(VS_ERR_ALIAS, "delta overlaps an input");
-    const dim3 grid(static_cast<unsigned>((seqlen + kThreads - 1) / kThreads), static_cast<unsigned>(dim),
-                    static_cast<unsigned>(batch));
+    const int64_t per_wg = static_cast<int64_t>(kThreads) * kDtTok;
+    const dim3 grid(static_cast<unsigned>((seqlen + per_wg - 1) / per_wg),
+                    static_cast<unsigned>((dim + kDtCh - 1) / kDtCh), static_cast<unsigned>(batch));
     hipLaunchKernelGGL(dt_proj_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), dt, w,
                        static_cast<uint16_t*>(delta), static_cast<int>(dim), static_cast<int>(seqlen));
     const hipError_t e = hipGetLastError();
