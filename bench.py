@@ -220,6 +220,7 @@ def main():
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_avg_s = float(np.mean(kern_ms)) * 1e-3
     ms_per_step = wall * 1e3 / args.steps
+    copy_gbs = copy_ceiling(torch, dev)
 
     tc = wl.tokens_channels
     value = tc / (ms_per_step * 1e-3) / 1e9
@@ -272,6 +273,7 @@ def main():
             "frac": round(upd_rate / UPDATE_PEAK, 4),
             "traffic": traffic,
         },
+        "kernel_ms_p10_p50_p90": [round(float(v), 5) for v in np.percentile(kern_ms, [10, 50, 90])],
         "roofline_hbm": {
             "bound": "hbm",
             "achieved": round(hbm_gbs, 1),
@@ -279,6 +281,8 @@ def main():
             "unit": "GB/s",
             "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes": alg_bytes,
+            "copy_ceiling": round(copy_gbs, 1),
+            "frac_of_copy": round(hbm_gbs / copy_gbs, 4),
         },
     }
     if not args.no_cpu_baseline:
@@ -402,6 +406,7 @@ def proj_bench(args, torch, dev):
     _, _, dt = vms.vim_x_proj(y0, Wx, N)
     d_ms = timed(lambda i: vms.vim_dt_proj(dt, wdt), args.steps)
 
+    copy_gbs = copy_ceiling(torch, dev)
     flops = 2.0 * batch * dim * dim * L
     tflops = flops / (kern_ms * 1e-3) / 1e12
     alg_bytes = 3 * batch * dim * L * 2 + dim * dim * 2 + dim * 4   # y, residual, out, W, bias
@@ -440,7 +445,8 @@ def proj_bench(args, torch, dev):
                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic},
         "roofline_hbm": {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
-                         "algorithmic_bytes": alg_bytes},
+                         "algorithmic_bytes": alg_bytes, "copy_ceiling": round(copy_gbs, 1),
+                         "frac_of_copy": round(hbm_gbs / copy_gbs, 4)},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = proj_cpu_baseline(sets[0]["y"], Wo, bias, sets[0]["r"])
@@ -463,6 +469,23 @@ def proj_cpu_baseline(y, W, bias, r, tokens=256):
             "seconds": round(dt, 3),
             "sample": "out_proj on %d batch rows x %d tokens, fp64, %s" % (
                 ys.shape[0], ys.shape[2], platform.machine())}
+
+
+def copy_ceiling(torch, dev, nbytes=512 << 20, reps=10):
+    """Measured HBM ceiling: GB/s (bytes read + written) of a plain device
+    copy of nbytes, timed with HIP events after one untimed copy."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    e1.synchronize()
+    gbs = 2.0 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    return gbs
 
 
 def copy_probe(torch, dev):
