@@ -87,9 +87,9 @@ def kernel_hash(path=KERNEL_SRC):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (batch, channel) scan is independent; see DESIGN.md for how it would "
-              "shard). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path. Every "
+              "(batch, channel) scan is independent, so splitting batch x channels across "
+              "GPUs would need no communication. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

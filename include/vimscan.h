@@ -68,7 +68,7 @@ enum {
     VS_ERR_DTYPE = -3,       /* unknown dtype */
     VS_ERR_ALIGN = -4,       /* a pointer is not aligned to its element size */
     VS_ERR_ALIAS = -5,       /* y overlaps an input or the workspace */
-    VS_ERR_UNSUPPORTED = -6, /* valid but not supported by this build (e.g. dstate > 16) */
+    VS_ERR_UNSUPPORTED = -6, /* valid but not supported by the library (e.g. dstate > 16) */
     VS_ERR_HIP = -7,         /* the HIP runtime reported an error (see vs_last_error) */
     VS_ERR_WORKSPACE = -8    /* workspace missing or smaller than vs_workspace_bytes() */
 };
