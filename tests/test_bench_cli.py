@@ -1,0 +1,31 @@
+"""bench.py's command-line contract that can be checked without a GPU: it
+measures one GPU and refuses more before touching any device, and its
+traffic records name the hash of the kernel source they were taken with
+(bench.py reports a record only while that hash matches)."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_records_name_their_kernel_source():
+    import bench
+    with open(bench.PROFILE_TRAFFIC) as f:
+        records = json.load(f)
+    assert "vim_s_1024_bf16" in records
+    for name, rec in records.items():
+        assert rec["bytes_per_launch"] > 0, name
+        assert len(rec["kernel_sha"]) == 16, name
+        assert rec["fetch_scale"] > 0 and rec["write_scale"] > 0, name
+
