@@ -1,0 +1,94 @@
+"""The scan entry points allocate nothing and issue only kernel launches, so
+a caller can capture them in a HIP graph. Each graph below is replayed
+several times, with eager work and synchronisations in between, and every
+replay must reproduce the eager call bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import say, upload
+from vision_mamba_selective_amd import workloads as wlm
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+
+def replay_and_check(run, eager, what):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = run()
+    for r in range(REPLAYS):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "%s: replay %d differs from the eager call" % (what, r)
+        # eager work between replays
+        torch.cuda.synchronize()
+        _ = run()
+        torch.cuda.synchronize()
+    say("  %s: %d replays equal the eager call" % (what, REPLAYS))
+
+
+@pytest.mark.parametrize("base", [wlm.WORKLOADS[0], wlm.WORKLOADS[1]], ids=["f32", "bf16"])
+def test_vim_scan_in_a_graph(base):
+    import vision_mamba_selective_amd as vms
+    wl = base.with_(batch=2, dim=24, seqlen=197)
+    t = upload(wlm.make_inputs(wl, random_A=True, random_D=True))
+    ws = torch.empty(max(1, vms.workspace_bytes(0, wl.batch, wl.dim, wl.seqlen, t["u"].dtype)),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(t["u"])
+
+    def run():
+        return vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
+                                  t["dt_bias"], out=y, workspace=ws)
+
+    eager = run().clone()
+    torch.cuda.synchronize()
+    say("case graph vim %s" % wl.dtype)
+    replay_and_check(run, eager, "vim_scan_bidir")
+
+
+def test_cross_scan_in_a_graph():
+    import vision_mamba_selective_amd as vms
+    wl = wlm.WORKLOADS[3].with_(batch=2, dim=8, H=13, W=21, seqlen=13 * 21)
+    t = upload(wlm.make_inputs(wl, random_A=True, random_D=True))
+    ws = torch.empty(vms.workspace_bytes(1, wl.batch, wl.dim, wl.seqlen, t["u"].dtype),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(t["u"])
+
+    def run():
+        return vms.vmamba_cross_scan4(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], wl.H, wl.W,
+                                      t["Dskip"], t["dt_bias"], out=y, workspace=ws)
+
+    eager = run().clone()
+    torch.cuda.synchronize()
+    say("case graph cross4")
+    replay_and_check(run, eager, "vmamba_cross_scan4")
+
+
+def test_gradient_in_a_graph():
+    """The gradient's launches include fill kernels that zero its summed
+    outputs; they are kernels, not memset nodes. dA, dD and ddt_bias are
+    summed with atomics in any order, so the bitwise check covers the
+    per-token outputs and the fixed-order dB, dC sums."""
+    import vision_mamba_selective_amd as vms
+    wl = wlm.WORKLOADS[1].with_(batch=2, dim=24, seqlen=70)
+    inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+    t = upload(inp)
+    dy = torch.from_numpy(wlm.round_bf16(np.random.default_rng(5).standard_normal(inp.u.shape)
+                                         .astype(np.float32))).cuda().to(torch.bfloat16)
+    ws = torch.empty(vms.workspace_bytes(3, wl.batch, wl.dim, wl.seqlen, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def run():
+        g = vms.vim_scan_bidir_grad(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
+                                    t["dt_bias"], dy, workspace=ws)
+        return torch.cat([g["du"].float().flatten(), g["ddelta"].float().flatten(),
+                          g["dz"].float().flatten(), g["dB"].flatten(), g["dC"].flatten()])
+
+    eager = run().clone()
+    torch.cuda.synchronize()
+    say("case graph gradient")
+    replay_and_check(run, eager, "vim_scan_bidir_grad")
