@@ -92,3 +92,22 @@ def test_gradient_in_a_graph():
     torch.cuda.synchronize()
     say("case graph gradient")
     replay_and_check(run, eager, "vim_scan_bidir_grad")
+
+
+def test_out_proj_in_a_graph():
+    import vision_mamba_selective_amd as vms
+    rng = np.random.default_rng(11)
+    bf = lambda a: torch.from_numpy(wlm.round_bf16(a.astype(np.float32))).cuda().to(torch.bfloat16)
+    y = bf(rng.standard_normal((2, 96, 197)))
+    W = bf(rng.standard_normal((96, 96)) / np.sqrt(96))
+    bias = torch.from_numpy(rng.standard_normal(96).astype(np.float32)).cuda()
+    res = bf(rng.standard_normal((2, 96, 197)))
+    out = torch.empty_like(y)
+
+    def run():
+        return vms.vim_out_proj(y, W, bias, res, out=out)
+
+    eager = run().clone()
+    torch.cuda.synchronize()
+    say("case graph out_proj")
+    replay_and_check(run, eager, "vim_out_proj")
