@@ -257,3 +257,23 @@ def test_python_binding_checks_shapes_before_calling():
     with pytest.raises(TypeError):
         scan.vim_scan_bidir(u.double(), u, None, torch.zeros(1, 16, 10), torch.zeros(1, 16, 10),
                             torch.zeros(2, 4, 16))
+
+
+def test_last_error_is_per_thread(nat):
+    """The detailed error text is kept per calling thread: a validation
+    failure in one thread leaves another thread's text empty."""
+    import threading
+    seen = {}
+
+    def bad():
+        seen["bad"] = (vim_call(nat, batch=0), nat.lib.vs_last_error())
+
+    def fresh():
+        seen["fresh"] = nat.lib.vs_last_error()
+
+    for fn in (bad, fresh):
+        t = threading.Thread(target=fn)
+        t.start()
+        t.join()
+    assert seen["bad"][0] == -2 and seen["bad"][1] != b""
+    assert seen["fresh"] == b""
