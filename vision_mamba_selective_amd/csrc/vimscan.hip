@@ -1188,9 +1188,9 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void grid_transpose_kernel(
     const T* __restrict__ u, const T* __restrict__ dl, T* __restrict__ uT, T* __restrict__ dT,
     int H, int W, int64_t nrows) {
-    __shared__ T tr[kTr][kTr + 1];
-    const T* __restrict__ src = blockIdx.z ? dl : u;
-    T* __restrict__ dst = blockIdx.z ? dT : uT;
+    // u's and delta's tile of the same (batch, channel) row in one
+    // workgroup: all 8 loads of a thread are issued before the barrier
+    __shared__ T tr[2][kTr][kTr + 1];
     const int tiles_w = (W + kTr - 1) / kTr;
     const int i0 = (blockIdx.x / tiles_w) * kTr, j0 = (blockIdx.x % tiles_w) * kTr;
     const int tx = threadIdx.x & (kTr - 1), ty = threadIdx.x / kTr;
@@ -1200,13 +1200,19 @@ __global__ __launch_bounds__(kThreads) void grid_transpose_kernel(
 #pragma unroll
         for (int r = ty; r < kTr; r += kThreads / kTr) {
             const int i = i0 + r, j = j0 + tx;
-            if (i < H && j < W) tr[r][tx] = src[base + static_cast<int64_t>(i) * W + j];
+            if (i < H && j < W) {
+                tr[0][r][tx] = u[base + static_cast<int64_t>(i) * W + j];
+                tr[1][r][tx] = dl[base + static_cast<int64_t>(i) * W + j];
+            }
         }
         __syncthreads();
 #pragma unroll
         for (int r = ty; r < kTr; r += kThreads / kTr) {
             const int j = j0 + r, i = i0 + tx;
-            if (i < H && j < W) dst[base + static_cast<int64_t>(j) * H + i] = tr[tx][r];
+            if (i < H && j < W) {
+                uT[base + static_cast<int64_t>(j) * H + i] = tr[0][tx][r];
+                dT[base + static_cast<int64_t>(j) * H + i] = tr[1][tx][r];
+            }
         }
         __syncthreads();
     }
@@ -1353,7 +1359,7 @@ int launch_t(const Call& c) {
         const int64_t rows = c.batch * c.dim;
         const unsigned tiles = static_cast<unsigned>(((c.H + kTr - 1) / kTr) * ((c.W + kTr - 1) / kTr));
         const unsigned gy = static_cast<unsigned>(rows < 65535 ? rows : 65535);
-        hipLaunchKernelGGL((grid_transpose_kernel<T>), dim3(tiles, gy, 2), blk, 0, st,
+        hipLaunchKernelGGL((grid_transpose_kernel<T>), dim3(tiles, gy, 1), blk, 0, st,
                            static_cast<const T*>(c.u), static_cast<const T*>(c.delta),
                            const_cast<T*>(static_cast<const T*>(a.uT)),
                            const_cast<T*>(static_cast<const T*>(a.deltaT)), c.H, c.W, rows);
