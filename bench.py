@@ -25,15 +25,34 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-#: MI355X published peaks
+#: MI355X published peaks and unit counts
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3          # published fp32 vector peak (packed FMA)
 CU = 256
+SIMDS_PER_CU = 4
+LANES_PER_SIMD = 16               # a wave64 VALU instruction issues over 4 cycles
 CLOCK_HZ = 2.4e9
-FP32_LANE_OPS = CU * 128 * CLOCK_HZ       # 157.3 TFLOP/s fp32 vector = 78.6 T lane-FMA/s
-#: VALU issue slots one state update needs at minimum: exp (quarter rate, 4)
-#: + delta*A, (delta*u)*B, the state FMA and the C*h FMA (1 each)
-SLOTS_PER_UPDATE = 8
-UPDATE_PEAK = FP32_LANE_OPS / SLOTS_PER_UPDATE   # 9.83e12 state updates / s
+#: VALU issue slots per second with non-packed fp32 instructions (the build
+#: keeps packed fp32 forms out): 256 x 4 x 16 x 2.4 GHz = 39.3e12. The
+#: published 157.3 TFLOP/s is this rate x 2 (FMA) x 2 (packed).
+LANE_SLOTS = CU * SIMDS_PER_CU * LANES_PER_SIMD * CLOCK_HZ
+#: arithmetic of one state update of the forward scan: delta*A (1 flop),
+#: (delta u)*B (1), the state FMA (2) and C*h (1) plus its share of the sum
+#: over the 16 states (1); the exp is not a flop
+FLOPS_PER_UPDATE = 6
+#: issue slots one forward state update needs at least: exp (a transcendental
+#: issues in 2 slots, by the counters), delta*A, (delta u)*B, the state FMA,
+#: C*h (1 each), and 15 adds per 16 states for the read-out sum
+SLOTS_PER_UPDATE = 2 + 4 + 15 / 16
+UPDATE_PEAK = LANE_SLOTS / SLOTS_PER_UPDATE      # 5.67e12 state updates / s
+#: the gradient per state update: the recomputed forward (delta*A, (delta u)*B,
+#: state FMA: 4 flops + exp), the adjoint lam = gs*C + e*lam (3), q = lam*h*e
+#: (2), the dA FMA (2), lam*B and q*A with their sums over states (4), and the
+#: dB, dC products (2) with the pair sum (1)
+GRAD_FLOPS_PER_UPDATE = 18
+#: its issue slots: exp (2) plus one slot per multiply, FMA and add above
+#: (16 operations; the two state sums are 15 adds per 16 states)
+GRAD_SLOTS_PER_UPDATE = 2 + 16
 
 #: dense bf16 matrix-core peak (no sparsity)
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -252,12 +271,16 @@ def main():
 
     tc = wl.tokens_channels
     value = tc / (ms_per_step * 1e-3) / 1e9
-    alg_bytes = wl.algorithmic_bytes()
+    alg_bytes = wl.grad_algorithmic_bytes() if args.grad else wl.algorithmic_bytes()
     if args.dirs:   # the second copies of u, delta, B and C
         alg_bytes += 2 * tc * wl.act_bytes + 2 * wl.batch * wl.dstate * wl.seqlen * wl.act_bytes
     hbm_gbs = alg_bytes / kern_avg_s / 1e9
     updates = wl.state_updates
     upd_rate = updates / kern_avg_s
+    flops_per_update = GRAD_FLOPS_PER_UPDATE if args.grad else FLOPS_PER_UPDATE
+    slots_per_update = GRAD_SLOTS_PER_UPDATE if args.grad else SLOTS_PER_UPDATE
+    tflops = flops_per_update * upd_rate / 1e12
+    upd_peak = LANE_SLOTS / slots_per_update
 
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
@@ -294,13 +317,26 @@ def main():
                    "launch": "one by one" if args.eager else "one HIP graph of the timed steps"},
         "hbm_GBps": round(hbm_gbs, 1),
         "kernel_ms": round(kern_avg_s * 1e3, 5),
+        # the arithmetic rate against the published fp32 vector peak
         "roofline": {
             "bound": "alu",
-            "achieved": round(upd_rate / 1e12, 4),
-            "peak": round(UPDATE_PEAK / 1e12, 4),
-            "unit": "Tupdate/s",
-            "frac": round(upd_rate / UPDATE_PEAK, 4),
+            "achieved": round(tflops, 3),
+            "peak": FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / FP32_PEAK_TFLOPS, 4),
             "traffic": traffic,
+            "flops_per_update": flops_per_update,
+        },
+        # the same rate against the issue-slot ceiling derived from the unit
+        # counts for non-packed fp32 VALU code (exp in 2 slots)
+        "roofline_issue": {
+            "achieved": round(upd_rate / 1e12, 4),
+            "peak": round(upd_peak / 1e12, 4),
+            "unit": "Tupdate/s",
+            "frac": round(upd_rate / upd_peak, 4),
+            "slots_per_update": round(slots_per_update, 4),
+            "lane_slots_per_s": LANE_SLOTS,
+            "clock_hz": CLOCK_HZ,
         },
         "kernel_ms_p10_p50_p90": [round(float(v), 5) for v in np.percentile(kern_ms, [10, 50, 90])],
         "roofline_hbm": {

@@ -96,7 +96,8 @@ enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 }
  * directions); an fp32 y serves as the first, so fp32 needs one fewer.
  * VS_OP_CROSS4 also holds column-major copies of u and delta (2 E elements
  * of the input dtype). VS_OP_1D needs none. Returns 0 for invalid
- * arguments. */
+ * arguments and for batch*dim*seqlen of 2^30 or more, which every entry
+ * point refuses (VS_ERR_UNSUPPORTED). */
 size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);
 
 /*

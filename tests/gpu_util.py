@@ -16,6 +16,16 @@ TOL = {wlm.F32: 1e-4, wlm.BF16: 2e-2}
 #: arithmetic of the scan relative to its typical size.
 STRICT = {wlm.F32: 1e-5, wlm.BF16: 2e-5}
 _SIG_BITS = {wlm.F32: None, wlm.BF16: 8}
+#: sequence length at which STRICT was set
+_STRICT_L = 300
+
+
+def strict_bound(dtype, L):
+    """STRICT for a sequence of L steps: each step rounds the state (the FMA
+    and the hardware exp2, about 2^-24 relative each) and those errors add up
+    over the steps the state remembers, like a random walk, so the bound grows
+    as sqrt(L) past the length at which STRICT was set."""
+    return STRICT[dtype] * max(1.0, (L / _STRICT_L) ** 0.5)
 
 
 def half_ulp(ref, dtype):

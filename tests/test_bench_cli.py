@@ -29,3 +29,13 @@ def test_traffic_records_name_their_kernel_source():
         assert len(rec["kernel_sha"]) == 16, name
         assert rec["fetch_scale"] > 0 and rec["write_scale"] > 0, name
 
+
+
+def test_roofline_peaks_follow_from_unit_counts():
+    """The published fp32 vector peak is the non-packed issue rate times 2
+    (FMA) times 2 (packed); the issue-slot ceiling divides that issue rate by
+    the slots of one state update."""
+    import bench
+    assert abs(bench.LANE_SLOTS * 2 * 2 / 1e12 - bench.FP32_PEAK_TFLOPS) < 0.1
+    assert abs(bench.UPDATE_PEAK - bench.LANE_SLOTS / bench.SLOTS_PER_UPDATE) < 1.0
+    assert 6.9 < bench.SLOTS_PER_UPDATE < 7.0

@@ -109,18 +109,13 @@ def test_conv_identity_taps_equal_plain_scan_of_silu():
 
 
 def test_conv_workload_full_size():
-    """The Vim-S 1024x1024 workload with the front end, at full size; the
-    oracle recomputes sampled (batch, channel) rows."""
+    """The Vim-S 1024x1024 workload with the front end, at full size; every
+    element of y is compared with the oracle."""
     wl = wlm.WORKLOADS[2]
     say("case conv workload %s" % wl.name)
     inp = wlm.make_inputs(wl)
     w, cb = conv_params(wl.dim, seed=2024)
-    y = run(inp, w, cb)
-    batches = [0, wl.batch - 1]
-    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, 16).astype(int), [7, 8]]))
-    sub = wlm.channel_subset(inp, batches, ch)
-    ref = reference(sub, w[:, ch], cb[:, ch])
-    got = host64(y[batches][:, ch.tolist()])
-    err = assert_close(got, ref, wl.dtype, "conv full size")
-    say("  sampled max rel err %.3g" % err)
+    y = host64(run(inp, w, cb))
+    err = assert_close(y, reference(inp, w, cb), wl.dtype, "conv full size")
+    say("  max rel err %.3g over all %d outputs" % (err, y.size))
     assert torch_dtype(wl) == torch.bfloat16

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (STRICT, assert_close, host64, run_gpu, say, stable_without_softplus, strict_err, upload)
+from gpu_util import (STRICT, assert_close, host64, run_gpu, say, stable_without_softplus, strict_bound,
+                      strict_err, upload)
 from vision_mamba_selective_amd import workloads as wlm
 
 pytestmark = pytest.mark.gpu
@@ -146,18 +147,27 @@ def test_cross4_repeatable_and_in_bounds():
 
 
 # ---- the 64 x 64 grid workload at full size, in the launch configuration the
-# benchmark times; the oracle recomputes a sample of (batch, channel) rows.
+# benchmark times; every element of y is compared with the oracle.
 @pytest.mark.parametrize("base", [X4_F32, X4_BF16], ids=["f32", "bf16"])
 def test_cross4_workload_full_size(base):
     wl = base
     say("case workload %s %s" % (wl.name, wl.dtype))
     inp = wlm.make_inputs(wl)
-    y = run_gpu(inp)
-    batches = sorted({0, wl.batch - 1})
-    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, 20).astype(int),
-                                   [3, 4, wl.dim - 1]]))
-    sub = wlm.channel_subset(inp, batches, ch)
-    ref = oracle.run_inputs(sub)
-    got = host64(y[batches][:, ch.tolist()])
-    err = assert_close(got, ref, wl.dtype, wl.name)
-    say("  %s sampled max rel err %.3g" % (wl.name, err))
+    y = host64(run_gpu(inp))
+    ref = oracle.run_inputs(inp)
+    err = assert_close(y, ref, wl.dtype, wl.name)
+    say("  %s max rel err %.3g over all %d outputs" % (wl.name, err, y.size))
+
+
+def test_cross4_scan_only_strict_full_size():
+    """D = 0, no gate, random A on the full 64 x 64 grid (fp32): the four
+    orders' carries over 4,096 steps each, with nothing to hide under."""
+    wl = X4_F32.with_(gate=False)
+    say("case cross4 scan-only strict full size")
+    inp = wlm.make_inputs(wl, random_A=True)
+    inp.D[:] = 0.0
+    y = host64(run_gpu(inp))
+    ref = oracle.run_inputs(inp)
+    err, rms = strict_err(y, ref, wl.dtype)
+    say("  max |dy| / rms = %.3g (rms %.3g)" % (err, rms))
+    assert err <= strict_bound(wl.dtype, wl.seqlen)

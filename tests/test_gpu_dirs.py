@@ -83,17 +83,11 @@ def test_dirs_identical_copies_equal_shared_scan():
 
 
 def test_dirs_workload_full_size():
-    """Vim-S 1024x1024 with per-direction inputs at full size; the oracle
-    recomputes sampled (batch, channel) rows."""
+    """Vim-S 1024x1024 with per-direction inputs at full size; every element
+    of y is compared with the oracle."""
     wl = wlm.WORKLOADS[2]
     x = dir_inputs(wl, random=False)
     say("case dirs workload %s" % wl.name)
-    y = run(wl, x)
-    batches = [0, wl.batch - 1]
-    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, 16).astype(int), [7, 8]]))
-    sub = dict(u=x["u"][:, batches][:, :, ch], delta=x["delta"][:, batches][:, :, ch],
-               z=x["z"][batches][:, ch], B=x["B"][batches], C=x["C"][batches],
-               A=x["A"][:, ch], D=x["D"][:, ch], dt_bias=x["dt_bias"][:, ch])
-    got = host64(y[batches][:, ch.tolist()])
-    err = assert_close(got, reference(sub), wl.dtype, "dirs full size")
-    say("  sampled max rel err %.3g" % err)
+    y = host64(run(wl, x))
+    err = assert_close(y, reference(x), wl.dtype, "dirs full size")
+    say("  max rel err %.3g over all %d outputs" % (err, y.size))

@@ -5,7 +5,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (STRICT, assert_close, host64, run_gpu, say, stable_without_softplus, strict_err, upload)
+from gpu_util import (STRICT, assert_close, host64, run_gpu, say, stable_without_softplus, strict_bound,
+                      strict_err, upload)
 from vision_mamba_selective_amd import workloads as wlm
 
 pytestmark = pytest.mark.gpu
@@ -123,23 +124,30 @@ def test_s6_1d(reverse, base):
 
 
 # ---- the workloads at full size, in the launch configuration the benchmark
-# times; the oracle recomputes a sample of (batch, channel) rows.
-def sample_rows(wl, nch=24):
-    batches = sorted({0, wl.batch - 1})
-    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, nch).astype(int),
-                                   [7, 8, wl.dim - 1]]))
-    return batches, ch
-
-
+# times. Every element of y is compared with the oracle, which takes about a
+# second per workload on the host's cores.
 @pytest.mark.parametrize("idx", [0, 1, 2, 4, 5])
 def test_vim_workload_full_size(idx):
     wl = wlm.WORKLOADS[idx]
     say("case workload %d %s" % (idx, wl.name))
     inp = wlm.make_inputs(wl)
-    y = run_gpu(inp)
-    batches, ch = sample_rows(wl)
-    sub = wlm.channel_subset(inp, batches, ch)
-    ref = oracle.run_inputs(sub)
-    got = host64(y[batches][:, ch.tolist()])
-    err = assert_close(got, ref, wl.dtype, wl.name)
-    say("  %s sampled max rel err %.3g" % (wl.name, err))
+    y = host64(run_gpu(inp))
+    ref = oracle.run_inputs(inp)
+    err = assert_close(y, ref, wl.dtype, wl.name)
+    say("  %s max rel err %.3g over all %d outputs" % (wl.name, err, y.size))
+
+
+@pytest.mark.parametrize("idx", [2, 4])
+def test_vim_scan_only_strict_full_length(idx):
+    """The strict scan-only check (D = 0, no gate, random A) at the full
+    sequence lengths of Vim-S 1024^2 and Vim-B 2048^2: a carry error over
+    thousands of steps cannot hide under the D*u term here."""
+    wl = wlm.WORKLOADS[idx].with_(gate=False)
+    say("case scan-only strict full length %s" % wl.name)
+    inp = wlm.make_inputs(wl, random_A=True)
+    inp.D[:] = 0.0
+    y = host64(run_gpu(inp))
+    ref = oracle.run_inputs(inp)
+    err, rms = strict_err(y, ref, wl.dtype)
+    say("  max (|dy| - output rounding) / rms = %.3g (rms %.3g, L %d)" % (err, rms, wl.seqlen))
+    assert err <= strict_bound(wl.dtype, wl.seqlen)

@@ -106,7 +106,8 @@ def test_zoh_1d_both_directions():
 
 
 def test_zoh_workload_full_size():
-    """Vim-S 1024x1024 with the exact hold, sampled (batch, channel) rows."""
+    """Vim-S 1024x1024 with the exact hold at full size; every element of y
+    is compared with the oracle."""
     import vision_mamba_selective_amd as vms
     wl = wlm.WORKLOADS[2]
     inp = wlm.make_inputs(wl)
@@ -114,9 +115,6 @@ def test_zoh_workload_full_size():
     say("case zoh workload %s" % wl.name)
     y = vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
                            t["dt_bias"], zoh=True)
-    batches = [0, wl.batch - 1]
-    ch = np.unique(np.concatenate([np.linspace(0, wl.dim - 1, 16).astype(int), [7, 8]]))
-    sub = wlm.channel_subset(inp, batches, ch)
-    got = host64(y[batches][:, ch.tolist()])
-    err = assert_close(got, oracle.run_inputs(sub, zoh=True), wl.dtype, "zoh full size")
-    say("  sampled max rel err %.3g" % err)
+    got = host64(y)
+    err = assert_close(got, oracle.run_inputs(inp, zoh=True), wl.dtype, "zoh full size")
+    say("  max rel err %.3g over all %d outputs" % (err, got.size))

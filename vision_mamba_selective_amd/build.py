@@ -9,7 +9,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "vimscan.hip")
-SRCS = [SRC, os.path.join(PKG, "csrc", "proj.hip")]
+SRCS = [SRC, os.path.join(PKG, "csrc", "proj.hip"), os.path.join(PKG, "csrc", "host.cpp")]
 LIB = os.path.join(PKG, "libvimscan.so")
 INCLUDE = os.path.join(ROOT, "include")
 

@@ -363,37 +363,22 @@ __global__ __launch_bounds__(kThreads) void dt_proj_kernel(const float* __restri
     }
 }
 
-bool overlap(const void* p, size_t np, const void* q, size_t nq) {
-    if (!p || !q || np == 0 || nq == 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(p), b0 = reinterpret_cast<uintptr_t>(q);
-    return a0 < b0 + nq && b0 < a0 + np;
-}
-bool al(const void* p, size_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
-
-int check_sizes(int64_t batch, int64_t M, int64_t K, int64_t L) {
-    if (batch < 1 || M < 1 || K < 1 || L < 1)
-        return vs_internal_fail(VS_ERR_SHAPE, "batch, feature counts and the sequence length must be >= 1");
-    if (batch > 65535) return vs_internal_fail(VS_ERR_SHAPE, "batch above 65535 is not supported");
-    if (M * K >= (int64_t(1) << 31) || batch * K * L >= (int64_t(1) << 31) ||
-        batch * M * L >= (int64_t(1) << 31) || L >= (int64_t(1) << 30))
-        return vs_internal_fail(VS_ERR_UNSUPPORTED, "tensors of 2^31 elements or more are not supported");
-    return VS_OK;
-}
+using vs::fail;
 
 template <int BM, int BN, int EPI>
 int launch(const ProjArgs& a, int64_t batch, hipStream_t st) {
     const int64_t tiles_l = (static_cast<int64_t>(a.L) + BN - 1) / BN;
     if (tiles_l > 65535)
-        return vs_internal_fail(VS_ERR_UNSUPPORTED, "sequence too long for the projection grid");
+        return fail(VS_ERR_UNSUPPORTED, "sequence too long for the projection grid");
     const dim3 grid(static_cast<unsigned>((a.M + BM - 1) / BM), static_cast<unsigned>(tiles_l),
                     static_cast<unsigned>(batch));
-    const bool wvec = a.K % 8 == 0 && al(a.W, 16);
+    const bool wvec = a.K % 8 == 0 && vs::aligned(a.W, 16);
     if (wvec)
         hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, EPI, true>), grid, dim3(kThreads), 0, st, a);
     else
         hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, EPI, false>), grid, dim3(kThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return vs_internal_fail(VS_ERR_HIP, hipGetErrorString(e));
+    if (e != hipSuccess) return fail(VS_ERR_HIP, hipGetErrorString(e));
     return VS_OK;
 }
 
@@ -403,29 +388,9 @@ extern "C" {
 
 int vim_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                const void* u, const void* W, void* B, void* C, float* dt, void* stream) {
-    vs_internal_clear_error();
-    if (dtype != VS_BF16)
-        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
-                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
-    if (dstate < 1 || dstate > VS_MAX_DSTATE)
-        return vs_internal_fail(dstate < 1 ? VS_ERR_SHAPE : VS_ERR_UNSUPPORTED, "dstate must be in 1..16");
-    const int64_t M = 2 * dstate + 1;
-    int rc = check_sizes(batch, M, dim, seqlen);
+    const int rc = vs::validate_x_proj(batch, dim, dstate, seqlen, dtype, u, W, B, C, dt);
     if (rc != VS_OK) return rc;
-    if (!u || !W || !B || !C || !dt) return vs_internal_fail(VS_ERR_NULL, "u, W, B, C and dt must not be NULL");
-    if (!al(u, 2) || !al(W, 2) || !al(B, 2) || !al(C, 2) || !al(dt, 4))
-        return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
-    const size_t nu = static_cast<size_t>(batch * dim * seqlen) * 2, nw = static_cast<size_t>(M * dim) * 2;
-    const size_t nbc = static_cast<size_t>(batch * dstate * seqlen) * 2, ndt = static_cast<size_t>(batch * seqlen) * 4;
-    const void* outs[] = {B, C, dt};
-    const size_t out_b[] = {nbc, nbc, ndt};
-    for (int i = 0; i < 3; ++i) {
-        if (overlap(outs[i], out_b[i], u, nu) || overlap(outs[i], out_b[i], W, nw))
-            return vs_internal_fail(VS_ERR_ALIAS, "an output overlaps an input");
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], out_b[i], outs[j], out_b[j]))
-                return vs_internal_fail(VS_ERR_ALIAS, "outputs overlap each other");
-    }
+    const int64_t M = 2 * dstate + 1;
     ProjArgs a{};
     a.W = static_cast<const uint16_t*>(W);
     a.X = static_cast<const uint16_t*>(u);
@@ -439,50 +404,23 @@ int vim_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int d
 
 int vim_dt_proj(int64_t batch, int64_t dim, int64_t seqlen, int dtype, const float* dt,
                 const float* w, void* delta, void* stream) {
-    vs_internal_clear_error();
-    if (dtype != VS_BF16)
-        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
-                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
-    int rc = check_sizes(batch, dim, 1, seqlen);
+    const int rc = vs::validate_dt_proj(batch, dim, seqlen, dtype, dt, w, delta);
     if (rc != VS_OK) return rc;
-    if (dim > 65535) return vs_internal_fail(VS_ERR_UNSUPPORTED, "dim above 65535 is not supported");
-    if (!dt || !w || !delta) return vs_internal_fail(VS_ERR_NULL, "dt, w and delta must not be NULL");
-    if (!al(dt, 4) || !al(w, 4) || !al(delta, 2)) return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
-    const size_t nd = static_cast<size_t>(batch * dim * seqlen) * 2;
-    if (overlap(delta, nd, dt, static_cast<size_t>(batch * seqlen) * 4) ||
-        overlap(delta, nd, w, static_cast<size_t>(dim) * 4))
-        return vs_internal_fail(VS_ERR_ALIAS, "delta overlaps an input");
     const int64_t per_wg = static_cast<int64_t>(kThreads) * kDtTok;
     const dim3 grid(static_cast<unsigned>((seqlen + per_wg - 1) / per_wg),
                     static_cast<unsigned>((dim + kDtCh - 1) / kDtCh), static_cast<unsigned>(batch));
     hipLaunchKernelGGL(dt_proj_kernel, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), dt, w,
                        static_cast<uint16_t*>(delta), static_cast<int>(dim), static_cast<int>(seqlen));
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return vs_internal_fail(VS_ERR_HIP, hipGetErrorString(e));
+    if (e != hipSuccess) return fail(VS_ERR_HIP, hipGetErrorString(e));
     return VS_OK;
 }
 
 int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen, int dtype,
                  const void* y, const void* W, const float* bias, const void* residual, void* out,
                  void* stream) {
-    vs_internal_clear_error();
-    if (dtype != VS_BF16)
-        return dtype == VS_F32 ? vs_internal_fail(VS_ERR_UNSUPPORTED, "the projections take bf16 only")
-                               : vs_internal_fail(VS_ERR_DTYPE, "unknown dtype");
-    int rc = check_sizes(batch, dim_out, dim_in, seqlen);
+    const int rc = vs::validate_out_proj(batch, dim_in, dim_out, seqlen, dtype, y, W, bias, residual, out);
     if (rc != VS_OK) return rc;
-    if (!y || !W || !out) return vs_internal_fail(VS_ERR_NULL, "y, W and out must not be NULL");
-    if (!al(y, 2) || !al(W, 2) || !al(out, 2) || !al(residual, 2) || !al(bias, 4))
-        return vs_internal_fail(VS_ERR_ALIGN, "pointer misaligned");
-    const size_t no = static_cast<size_t>(batch * dim_out * seqlen) * 2;
-    if (overlap(out, no, y, static_cast<size_t>(batch * dim_in * seqlen) * 2) ||
-        overlap(out, no, W, static_cast<size_t>(dim_out * dim_in) * 2) ||
-        overlap(out, no, bias, static_cast<size_t>(dim_out) * 4))
-        return vs_internal_fail(VS_ERR_ALIAS, "out overlaps an input");
-    // out may be the residual itself (each element is read before it is
-    // written, by the same thread); any other overlap is refused
-    if (residual != out && overlap(out, no, residual, no))
-        return vs_internal_fail(VS_ERR_ALIAS, "out partly overlaps the residual");
     ProjArgs a{};
     a.W = static_cast<const uint16_t*>(W);
     a.X = static_cast<const uint16_t*>(y);

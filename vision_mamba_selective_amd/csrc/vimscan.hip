@@ -21,8 +21,10 @@
 //     state lane reads its own 16-token window.
 //   * The read-out sum over states (y = C . h) is a 16-lane transpose
 //     reduction inside the row after each block: lane j ends with token j.
-//   * Reverse and column-major orders are index arithmetic on the token
-//     address; nothing is flipped or transposed in memory.
+//   * Reverse orders are index arithmetic on the token address; nothing is
+//     flipped in memory. The VMamba column-major pair reads u and delta from
+//     column-major copies that a transpose pre-pass writes to the workspace
+//     (strided reads of the row-major grid measured 2.5x slower).
 //   * Directions that visit a token at different times meet through an fp32
 //     partial sum (a workspace, or y itself when y is fp32): the first
 //     direction to finish a token stores its contribution, the last one adds
@@ -41,15 +43,17 @@
 namespace {
 
 constexpr int kWaveLanes = 64;
-constexpr int kRowLanes = 16;       // one recurrence per DPP row
-constexpr int kBlockTok = 16;       // tokens per block step
+using vs::kRowLanes;                // one recurrence per DPP row
+using vs::kBlockTok;                // tokens per block step
 constexpr int kThreads = 256;       // 4 waves per workgroup
 constexpr int kTilePad = 20;        // LDS row stride (floats) of a 16-token tile
 constexpr int kTokAhead = 3;        // blocks the forward scan's token loads run ahead
 constexpr int kTr = 32;             // grid transpose tile edge
 constexpr int kTrPad = kTr + 1;
 
-enum Mode { kMode1D = 0, kModeVim = 1, kModeCross4 = 2 };
+using vs::kMode1D;
+using vs::kModeVim;
+using vs::kModeCross4;
 
 struct ScanArgs {
     const void* u;
@@ -785,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //     the workgroups in a fixed order, so no atomics are involved and dB and
 //     dC repeat bit for bit. dA, dD and dt_bias are summed per row and added
 //     once at the end with atomics.
-constexpr int kBcChunk = 1024;    // floats per workgroup and block: [dB|dC][side][n][step]
+using vs::kBcChunk;               // floats per workgroup and block: [dB|dC][side][n][step]
 
 struct GradArgs {
     const void *u, *delta, *z, *B, *C, *dy;
@@ -1219,97 +1223,11 @@ __global__ __launch_bounds__(kThreads) void grid_transpose_kernel(
 }
 
 // ---------------------------------------------------------------- host side
-thread_local std::string g_last_error;
-
-int fail(int code, const std::string& msg) {
-    g_last_error = msg;
-    return code;
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-    if (!a || !b || na == 0 || nb == 0) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
-    return a0 < b0 + nb && b0 < a0 + na;
-}
-
-bool aligned(const void* p, size_t al) { return (reinterpret_cast<uintptr_t>(p) % al) == 0; }
-
-struct Call {
-    int mode;
-    int64_t batch, dim, dstate, L;
-    int H, W;
-    int dtype;
-    int reverse;
-    const void *u, *delta, *z, *B, *C;
-    const float *A, *Dskip, *dt_bias;
-    int softplus;
-    void* y;
-    void* ws;
-    size_t ws_bytes;
-    void* stream;
-    const float* conv_w = nullptr;   // Vim front end (u then holds x)
-    const float* conv_b = nullptr;
-    bool per_dir = false;            // Vim: u, delta [2][batch][dim][L]; B, C [batch][2][N][L]
-    bool zoh = false;                // exact zero-order-hold B_bar
-};
-
-int64_t ndirs(int mode) { return mode == kModeVim ? 2 : (mode == kModeCross4 ? 4 : 1); }
-
-int validate(const Call& c) {
-    if (c.dtype != VS_F32 && c.dtype != VS_BF16) return fail(VS_ERR_DTYPE, "unknown dtype");
-    if (c.batch < 1 || c.dim < 1 || c.L < 1 || c.dstate < 1)
-        return fail(VS_ERR_SHAPE, "batch, dim, dstate and the sequence length must be >= 1");
-    if (c.dstate > VS_MAX_DSTATE)
-        return fail(VS_ERR_UNSUPPORTED, "dstate above 16 is not supported");
-    if (c.batch > 65535) return fail(VS_ERR_SHAPE, "batch above 65535 is not supported");
-    if (c.L > (int64_t(1) << 30) || c.dim > (int64_t(1) << 30))
-        return fail(VS_ERR_SHAPE, "sequence length or dim too large");
-    const int64_t elems = c.batch * c.dim * c.L;
-    // kernels address every tensor with 32-bit byte offsets (fp32 partial
-    // sums included), so each tensor must stay below 4 GiB
-    if (elems >= (int64_t(1) << 30) || c.batch * 4 * c.dstate * c.L >= (int64_t(1) << 30))
-        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
-    const int64_t copies = c.per_dir ? 2 : 1;     // direction copies of u, delta, B and C
-    if (copies * elems >= (int64_t(1) << 30))
-        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
-    if (!c.u || !c.delta || !c.B || !c.C || !c.A || !c.y)
-        return fail(VS_ERR_NULL, "u, delta, B, C, A and y must not be NULL");
-    const size_t es = c.dtype == VS_BF16 ? 2 : 4;
-    const void* acts[] = {c.u, c.delta, c.z, c.B, c.C, c.y};
-    for (const void* p : acts)
-        if (p && !aligned(p, es)) return fail(VS_ERR_ALIGN, "activation pointer misaligned");
-    const void* fparams[] = {c.A, c.Dskip, c.dt_bias, c.ws, c.conv_w, c.conv_b};
-    for (const void* p : fparams)
-        if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
-    const int64_t nd = ndirs(c.mode);
-    const size_t act = static_cast<size_t>(elems) * es;
-    const size_t bc = static_cast<size_t>(c.batch * (c.mode == kModeCross4 ? 4 : copies) *
-                                          c.dstate * c.L) * es;
-    const size_t act_in = act * static_cast<size_t>(copies);
-    const size_t a_bytes = static_cast<size_t>(nd * c.dim * c.dstate) * 4;
-    const size_t p_bytes = static_cast<size_t>(nd * c.dim) * 4;
-    const void* ins[] = {c.u, c.delta, c.z, c.B, c.C, c.A, c.Dskip, c.dt_bias, c.conv_w, c.conv_b};
-    const size_t in_bytes[] = {act_in, act_in, act, bc, bc, a_bytes, p_bytes, p_bytes, 3 * p_bytes,
-                               p_bytes};
-    constexpr int kIns = 10;
-    for (int i = 0; i < kIns; ++i)
-        if (overlaps(c.y, act, ins[i], in_bytes[i]))
-            return fail(VS_ERR_ALIAS, "y overlaps an input");
-    const size_t need = vs_workspace_bytes(
-        c.mode == kModeVim ? VS_OP_VIM_BIDIR : (c.mode == kModeCross4 ? VS_OP_CROSS4 : VS_OP_1D),
-        c.batch, c.dim, c.L, c.dtype);
-    if (need > 0) {
-        if (!c.ws || c.ws_bytes < need)
-            return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
-        if (overlaps(c.y, act, c.ws, need)) return fail(VS_ERR_ALIAS, "y overlaps the workspace");
-        for (int i = 0; i < kIns; ++i)
-            if (overlaps(c.ws, need, ins[i], in_bytes[i]))
-                return fail(VS_ERR_ALIAS, "workspace overlaps an input");
-    }
-    if (c.mode == kModeCross4 && (c.H < 1 || c.W < 1 || int64_t(c.H) * c.W != c.L))
-        return fail(VS_ERR_SHAPE, "H and W must be >= 1 with H*W = L");
-    return VS_OK;
-}
+// Argument records and their validation live in host.cpp (vs_internal.h);
+// this file launches the kernels for calls that passed it.
+using vs::Call;
+using vs::GradCall;
+using vs::fail;
 
 template <typename T, int MODE, bool CONV, bool ZOH>
 void launch_scan(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a) {
@@ -1383,102 +1301,9 @@ int launch_t(const Call& c) {
     return VS_OK;
 }
 
-// ---- gradient of the Vim scan
-struct GradCall {
-    int64_t batch, dim, dstate, L;
-    int dtype;
-    const void *u, *delta, *z, *B, *C;
-    const float *A, *Dskip, *dt_bias;
-    int softplus;
-    const void* dy;
-    void *du, *ddelta, *dz;
-    float *dB, *dC, *dA, *dD, *dbias;
-    void* ws;
-    size_t ws_bytes;
-    void* stream;
-};
-
-// workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
-// [du partials: fp32 E][ddelta partials: fp32 E], each 256-byte aligned
-// Channels per gradient workgroup. With 24 (768 threads, one workgroup per
-// CU at 3 waves per SIMD) the workgroups write a third of the dB/dC chunks
-// that 8 channels (256 threads) write; 24 is used when it still gives every
-// one of the 256 CUs a workgroup.
-constexpr int64_t kNumCUs = 256;
-int grad_channels(int64_t batch, int64_t dim) {
-    return batch * ((dim + 23) / 24) >= kNumCUs ? 24 : 8;
-}
-// the gradient kernel's buffer descriptors span two channels' rows in bytes
-// (2 L x 4 B), which must stay well inside a 32-bit signed range
-constexpr int64_t kGradMaxL = int64_t(1) << 26;
-size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
-    const size_t elems = static_cast<size_t>(batch * dim * L);
-    const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
-    const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
-    const int ch = grad_channels(batch, dim);
-    const size_t groups = static_cast<size_t>((dim + ch - 1) / ch);
-    const size_t chunks = static_cast<size_t>(batch) * groups * nblk * kBcChunk;
-    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    size_t off = 0;
-    offs[0] = off; off += al(4 * elems);     // merged ungated forward output
-    offs[1] = off; off += al(4 * ck);        // block-start states
-    offs[2] = off; off += al(4 * elems);     // du partials
-    offs[3] = off; off += al(4 * elems);     // ddelta partials
-    offs[4] = off; off += al(4 * chunks);    // dB/dC chunks
-    return off;
-}
-
-int validate_grad(const GradCall& g) {
-    if (g.dtype != VS_F32 && g.dtype != VS_BF16) return fail(VS_ERR_DTYPE, "unknown dtype");
-    if (g.softplus & ~VS_FLAG_SOFTPLUS)
-        return fail(VS_ERR_UNSUPPORTED, "the gradient takes VS_FLAG_SOFTPLUS only (delta B form)");
-    if (g.batch < 1 || g.dim < 1 || g.L < 1 || g.dstate < 1)
-        return fail(VS_ERR_SHAPE, "batch, dim, dstate and the sequence length must be >= 1");
-    if (g.dstate > VS_MAX_DSTATE)
-        return fail(VS_ERR_UNSUPPORTED, "dstate above 16 is not supported");
-    if (g.batch > 65535) return fail(VS_ERR_SHAPE, "batch above 65535 is not supported");
-    if (g.L > (int64_t(1) << 30) || g.dim > (int64_t(1) << 30))
-        return fail(VS_ERR_SHAPE, "sequence length or dim too large");
-    const int64_t elems = g.batch * g.dim * g.L;
-    if (elems >= (int64_t(1) << 30) || g.batch * g.dstate * g.L >= (int64_t(1) << 30))
-        return fail(VS_ERR_UNSUPPORTED, "tensors of 2^30 elements or more are not supported");
-    if (g.L > kGradMaxL) return fail(VS_ERR_UNSUPPORTED, "the gradient supports sequences of up to 2^26 tokens");
-    if (!g.u || !g.delta || !g.B || !g.C || !g.A || !g.dy)
-        return fail(VS_ERR_NULL, "u, delta, B, C, A and dy must not be NULL");
-    if (!g.du || !g.ddelta || !g.dB || !g.dC || !g.dA || !g.dD || !g.dbias)
-        return fail(VS_ERR_NULL, "every gradient output must be given");
-    if (g.z && !g.dz) return fail(VS_ERR_NULL, "dz must not be NULL when z is given");
-    const size_t es = g.dtype == VS_BF16 ? 2 : 4;
-    const void* acts[] = {g.u, g.delta, g.z, g.B, g.C, g.dy, g.du, g.ddelta, g.dz};
-    for (const void* p : acts)
-        if (p && !aligned(p, es)) return fail(VS_ERR_ALIGN, "activation pointer misaligned");
-    const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
-    for (const void* p : fps)
-        if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
-    size_t offs[5];
-    const size_t need = grad_ws_bytes(g.batch, g.dim, g.L, offs);
-    if (!g.ws || g.ws_bytes < need)
-        return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
-    // no output (nor the workspace) may overlap an input or another output
-    const size_t act = static_cast<size_t>(elems) * es;
-    const size_t bc_in = static_cast<size_t>(g.batch * g.dstate * g.L) * es;
-    const size_t bcf = static_cast<size_t>(g.batch * g.dstate * g.L) * 4;
-    const size_t pa = static_cast<size_t>(2 * g.dim * g.dstate) * 4;
-    const size_t pd = static_cast<size_t>(2 * g.dim) * 4;
-    const void* ins[] = {g.u, g.delta, g.z, g.B, g.C, g.A, g.Dskip, g.dt_bias, g.dy};
-    const size_t in_b[] = {act, act, act, bc_in, bc_in, pa, pd, pd, act};
-    const void* outs[] = {g.du, g.ddelta, g.dz, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
-    const size_t out_b[] = {act, act, act, bcf, bcf, pa, pd, pd, need};
-    for (int i = 0; i < 9; ++i) {
-        for (int j = 0; j < 9; ++j)
-            if (overlaps(outs[i], out_b[i], ins[j], in_b[j]))
-                return fail(VS_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
-        for (int j = i + 1; j < 9; ++j)
-            if (overlaps(outs[i], out_b[i], outs[j], out_b[j]))
-                return fail(VS_ERR_ALIAS, "gradient outputs overlap each other or the workspace");
-    }
-    return VS_OK;
-}
+// ---- gradient of the Vim scan (workspace layout: vs::grad_ws_bytes)
+using vs::grad_channels;
+using vs::grad_ws_bytes;
 
 template <typename T, int CH>
 void launch_rowgrad(bool gate, bool softplus, dim3 grid, hipStream_t st, const GradArgs& r) {
@@ -1553,13 +1378,7 @@ int launch_grad(const GradCall& g) {
 }
 
 int run(Call c) {
-    g_last_error.clear();
-    // the delta_softplus argument is a flags word: VS_FLAG_SOFTPLUS, VS_FLAG_ZOH
-    if (c.softplus & ~(VS_FLAG_SOFTPLUS | VS_FLAG_ZOH))
-        return fail(VS_ERR_UNSUPPORTED, "unknown flag bits");
-    c.zoh = (c.softplus & VS_FLAG_ZOH) != 0;
-    c.softplus &= VS_FLAG_SOFTPLUS;
-    int rc = validate(c);
+    int rc = vs::prepare(c);
     if (rc != VS_OK) return rc;
     const bool bf = c.dtype == VS_BF16;
     switch (c.mode) {
@@ -1571,31 +1390,8 @@ int run(Call c) {
 
 }  // namespace
 
-// the error record, for the projection kernels' translation unit
-int vs_internal_fail(int code, const char* msg) { return fail(code, msg); }
-void vs_internal_clear_error() { g_last_error.clear(); }
-
 // ---------------------------------------------------------------- C ABI
 extern "C" {
-
-size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype) {
-    if (batch < 1 || dim < 1 || seqlen < 1) return 0;
-    if (dtype != VS_F32 && dtype != VS_BF16) return 0;
-    if (op == VS_OP_VIM_GRAD) {
-        size_t offs[5];
-        return grad_ws_bytes(batch, dim, seqlen, offs);
-    }
-    // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
-    // cross-scan two; an fp32 y serves as the first. The cross-scan also
-    // keeps column-major copies of u and delta (input dtype).
-    const int64_t elems = batch * dim * seqlen;
-    const int64_t bufs = (op == VS_OP_VIM_BIDIR ? 1 : (op == VS_OP_CROSS4 ? 2 : 0)) -
-                         (dtype == VS_F32 ? 1 : 0);
-    const int64_t copies = op == VS_OP_CROSS4 ? 2 : 0;
-    const int64_t es = dtype == VS_BF16 ? 2 : 4;
-    if (bufs <= 0 && copies == 0) return 0;
-    return static_cast<size_t>(elems * (4 * (bufs > 0 ? bufs : 0) + es * copies));
-}
 
 int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
                    const void* u, const void* delta, const void* z, const void* B,
@@ -1623,12 +1419,9 @@ int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         const float* A, const float* Dskip, const float* dt_bias,
                         int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
                         void* stream) {
-    if (!conv_w) {
-        g_last_error = "conv_w must not be NULL";
-        return VS_ERR_NULL;
-    }
     Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, x, delta, z, B, C,
            A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    c.conv = true;
     c.conv_w = conv_w;
     c.conv_b = conv_b;
     return run(c);
@@ -1640,11 +1433,11 @@ int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         int delta_softplus, const void* dy, void* du, void* ddelta, void* dz,
                         float* dB, float* dC, float* dA, float* dD, float* ddt_bias,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    g_last_error.clear();
+    vs::clear_error();
     GradCall g{batch, dim, dstate, seqlen, dtype, u, delta, z, B, C, A, Dskip, dt_bias,
                delta_softplus, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
                workspace, workspace_bytes, stream};
-    const int rc = validate_grad(g);
+    const int rc = vs::validate_grad(g);
     if (rc != VS_OK) return rc;
     return dtype == VS_BF16 ? launch_grad<uint16_t>(g) : launch_grad<float>(g);
 }
@@ -1654,10 +1447,8 @@ int vmamba_cross_scan4(int64_t batch, int64_t dim, int64_t dstate, int64_t H, in
                        const void* B, const void* C, const float* A, const float* Dskip,
                        const float* dt_bias, int delta_softplus, void* y, void* workspace,
                        size_t workspace_bytes, void* stream) {
-    if (H < 1 || W < 1 || H > (int64_t(1) << 20) || W > (int64_t(1) << 20)) {
-        g_last_error = "H and W must be in 1..2^20";
-        return VS_ERR_SHAPE;
-    }
+    vs::clear_error();
+    if (!vs::grid_ok(H, W)) return fail(VS_ERR_SHAPE, "H and W must be in 1..2^20");
     Call c{kModeCross4, batch, dim, dstate, H * W, static_cast<int>(H), static_cast<int>(W),
            dtype, 0, u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus, y, workspace,
            workspace_bytes, stream};
@@ -1672,24 +1463,5 @@ int s6_scan_1d(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int d
            A, Dskip, dt_bias, delta_softplus, y, nullptr, 0, stream};
     return run(c);
 }
-
-const char* vs_strerror(int status) {
-    switch (status) {
-    case VS_OK: return "VS_OK";
-    case VS_ERR_NULL: return "VS_ERR_NULL";
-    case VS_ERR_SHAPE: return "VS_ERR_SHAPE";
-    case VS_ERR_DTYPE: return "VS_ERR_DTYPE";
-    case VS_ERR_ALIGN: return "VS_ERR_ALIGN";
-    case VS_ERR_ALIAS: return "VS_ERR_ALIAS";
-    case VS_ERR_UNSUPPORTED: return "VS_ERR_UNSUPPORTED";
-    case VS_ERR_HIP: return "VS_ERR_HIP";
-    case VS_ERR_WORKSPACE: return "VS_ERR_WORKSPACE";
-    default: return "VS_ERR_UNKNOWN";
-    }
-}
-
-const char* vs_last_error(void) { return g_last_error.c_str(); }
-
-int vs_abi_version(void) { return VS_ABI_VERSION; }
 
 }  // extern "C"

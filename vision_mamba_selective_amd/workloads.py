@@ -92,6 +92,20 @@ class Workload:
         params = self.ndir * self.dim * (self.dstate + 2) * 4
         return n_act * tc * e + bc + params
 
+    def grad_algorithmic_bytes(self) -> int:
+        """Bytes the gradient must move at minimum (Vim): read u, delta_raw,
+        (z), dy, B, C and the parameters once; write du, ddelta, (dz) in the
+        activation dtype, dB and dC in fp32 and the parameter gradients
+        once."""
+        e = self.act_bytes
+        tc = self.tokens_channels
+        g = 1 if self.gate else 0
+        bc = self.batch * self.dstate * self.seqlen
+        params = self.ndir * self.dim * (self.dstate + 2) * 4
+        reads = (3 + g) * tc * e + 2 * bc * e + params
+        writes = (2 + g) * tc * e + 2 * bc * 4 + params
+        return reads + writes
+
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
 
