@@ -123,6 +123,32 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* Largest batch*dim*seqlen that vim_scan_bidir_noalloc takes for bf16
+ * activations: its library-owned merge buffer holds this many fp32 values
+ * (128 MiB per GPU). fp32 activations need no buffer (y holds the partial
+ * sums) and take any size the other entry points take. */
+#define VS_NOALLOC_MAX_ELEMS (1 << 25)
+
+/*
+ * vim_scan_bidir for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts and result as vim_scan_bidir, without the
+ * workspace: the fp32 merge buffer is a static device array of the library
+ * (VS_NOALLOC_MAX_ELEMS floats), allocated when the library's code object is
+ * loaded on a GPU and held until the process ends. The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine). Each GPU has
+ * its own copy of the buffer, which every call on that GPU shares and which
+ * keeps the last call's contents (the scan needs no cleared buffer: every
+ * entry is written before it is read). Calls that overlap in time on one GPU
+ * (other streams, other host threads) race on the buffer: serialise them.
+ * Returns VS_ERR_UNSUPPORTED when the activations are bf16 and
+ * batch*dim*seqlen exceeds VS_NOALLOC_MAX_ELEMS, checked before any HIP call.
+ */
+int vim_scan_bidir_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                           const void* u, const void* delta, const void* z, const void* B,
+                           const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                           int delta_softplus, void* y, void* stream);
+
 /*
  * vim_scan_bidir with per-direction inputs. In the guide's block code
  * (section "1. PyTorch Implementation of the Bidirectional Vision Mamba

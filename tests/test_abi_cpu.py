@@ -277,3 +277,19 @@ def test_last_error_is_per_thread(nat):
         t.join()
     assert seen["bad"][0] == -2 and seen["bad"][1] != b""
     assert seen["fresh"] == b""
+
+
+def test_noalloc_refuses_sizes_beyond_its_buffer(nat):
+    """vim_scan_bidir_noalloc checks the size against its static buffer
+    before any HIP call: bf16 with batch*dim*L above VS_NOALLOC_MAX_ELEMS is
+    VS_ERR_UNSUPPORTED with a message naming the limit."""
+    f = nat.lib.vim_scan_bidir_noalloc
+    big = (8, 1024, 4097)                 # 33.6 M elements > 2^25
+    assert big[0] * big[1] * big[2] > nat.VS_NOALLOC_MAX_ELEMS
+    rc = f(*big[:2], 16, big[2], nat.VS_BF16, far(0), far(1), far(2), far(3), far(4), far(5),
+           far(6), far(7), 1, far(8), None)
+    assert rc == -6
+    assert b"no-allocation maximum" in nat.lib.vs_last_error()
+    rc = f(2, 8, 16, 33, nat.VS_BF16, None, far(1), far(2), far(3), far(4), far(5), far(6),
+           far(7), 1, far(8), None)
+    assert rc == -1

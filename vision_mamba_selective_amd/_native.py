@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libvimscan.so")
 
 VS_F32, VS_BF16 = 0, 1
 VS_OP_VIM_BIDIR, VS_OP_CROSS4, VS_OP_1D, VS_OP_VIM_GRAD = 0, 1, 2, 3
+VS_NOALLOC_MAX_ELEMS = 1 << 25
 
 # names and argument types of every entry point declared in include/vimscan.h
 _I64 = ctypes.c_int64
@@ -25,6 +26,8 @@ SIGNATURES = {
     "vs_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "vim_scan_bidir": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                             _P, _P, _SZ, _P]),
+    "vim_scan_bidir_noalloc": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _I, _P, _P]),
     "vim_scan_bidir_dirs": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                                  _P, _P, _SZ, _P]),
     "vim_scan_bidir_conv": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,

@@ -113,7 +113,13 @@ int validate(const Call& c) {
     const size_t need = scan_ws_bytes(
         c.mode == kModeVim ? VS_OP_VIM_BIDIR : (c.mode == kModeCross4 ? VS_OP_CROSS4 : VS_OP_1D),
         c.batch, c.dim, c.L, c.dtype);
-    if (need > 0) {
+    if (need > 0 && c.ws_internal) {
+        // the library's own buffer: no overlap with the caller's memory is
+        // possible, only its capacity can fall short
+        if (c.ws_bytes < need)
+            return fail(VS_ERR_UNSUPPORTED, "batch*dim*seqlen above the no-allocation maximum "
+                                            "(VS_NOALLOC_MAX_ELEMS for bf16)");
+    } else if (need > 0) {
         if (!c.ws || c.ws_bytes < need)
             return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
         if (overlaps(c.y, act, c.ws, need)) return fail(VS_ERR_ALIAS, "y overlaps the workspace");

@@ -34,6 +34,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1377,15 +1378,47 @@ int launch_grad(const GradCall& g) {
     return VS_OK;
 }
 
-int run(Call c) {
-    int rc = vs::prepare(c);
-    if (rc != VS_OK) return rc;
+// launches a call that passed vs::prepare
+int dispatch(const Call& c) {
     const bool bf = c.dtype == VS_BF16;
     switch (c.mode) {
     case kMode1D: return bf ? launch_t<uint16_t, kMode1D>(c) : launch_t<float, kMode1D>(c);
     case kModeVim: return bf ? launch_t<uint16_t, kModeVim>(c) : launch_t<float, kModeVim>(c);
     default: return bf ? launch_t<uint16_t, kModeCross4>(c) : launch_t<float, kModeCross4>(c);
     }
+}
+
+int run(Call c) {
+    const int rc = vs::prepare(c);
+    return rc != VS_OK ? rc : dispatch(c);
+}
+
+// ---- the merge buffer of vim_scan_bidir_noalloc: a static device array
+// (each GPU that loads the library holds its own copy until the process
+// ends). Host code never uses the array's name as an address: the device
+// address is looked up once per device with that device current and kept.
+constexpr size_t kScratchFloats = VS_NOALLOC_MAX_ELEMS;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];
+
+int scratch_on_current_device(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(VS_ERR_UNSUPPORTED, "device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(VS_ERR_HIP, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return VS_OK;
 }
 
 }  // namespace
@@ -1401,6 +1434,22 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
     Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
            A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
     return run(c);
+}
+
+int vim_scan_bidir_noalloc(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                           const void* u, const void* delta, const void* z, const void* B,
+                           const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                           int delta_softplus, void* y, void* stream) {
+    Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
+           A, Dskip, dt_bias, delta_softplus, y, nullptr, kScratchFloats * sizeof(float), stream};
+    c.ws_internal = true;
+    int rc = vs::prepare(c);        // sizes first: nothing below runs for a refused call
+    if (rc != VS_OK) return rc;
+    float* buf = nullptr;
+    rc = scratch_on_current_device(&buf);
+    if (rc != VS_OK) return rc;
+    c.ws = buf;
+    return dispatch(c);
 }
 
 int vim_scan_bidir_dirs(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,

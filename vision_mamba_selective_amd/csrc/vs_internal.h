@@ -43,6 +43,7 @@ struct Call {
     bool per_dir = false;           // Vim: u, delta [2][batch][dim][L]; B, C [batch][2][N][L]
     bool zoh = false;               // exact zero-order-hold B_bar
     int chunks = 0;                 // Vim: chunks per sequence (0: the library's choice)
+    bool ws_internal = false;       // the workspace is the library's own (ws_bytes = its capacity)
 };
 
 struct GradCall {
