@@ -93,6 +93,9 @@ def parse():
                    help="time the projections around the scan at the workload's shape: one step is "
                         "out_proj (dim -> dim, bias + residual) on the matrix cores; x_proj and "
                         "dt_proj are timed beside it")
+    p.add_argument("--chunks", type=int, default=None,
+                   help="time vim_scan_bidir_chunked with this many chunks per sequence (0: the "
+                        "library's choice, which is what the default line runs)")
     p.add_argument("--eager", action="store_true",
                    help="launch the timed steps one by one instead of replaying them as one HIP graph")
     p.add_argument("--copy-probe", action="store_true",
@@ -137,6 +140,10 @@ def main():
         sys.exit(2)
     if args.conv + args.grad + args.dirs > 1:
         print("--conv, --grad and --dirs are separate measurements", file=sys.stderr)
+        sys.exit(2)
+    if args.chunks is not None and (wl.kind != "vim" or args.conv or args.grad or args.dirs
+                                    or args.zoh):
+        print("--chunks applies to the plain Vim scan", file=sys.stderr)
         sys.exit(2)
     if args.zoh and args.grad:
         print("the gradient uses the delta B form; --zoh is a forward option", file=sys.stderr)
@@ -214,6 +221,10 @@ def main():
         elif args.dirs:
             vms.vim_scan_bidir_dirs(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
                                     t["bias"], out=t["y"], workspace=t["ws"], zoh=args.zoh)
+        elif wl.kind == "vim" and args.chunks is not None:
+            vms.vim_scan_bidir_chunked(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
+                                       t["bias"], chunks=args.chunks, out=t["y"],
+                                       workspace=t["ws"])
         elif wl.kind == "vim":
             vms.vim_scan_bidir(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["D"],
                                t["bias"], out=t["y"], workspace=t["ws"], zoh=args.zoh)
@@ -314,6 +325,7 @@ def main():
                    "pass": "gradient (forward recompute + adjoint)" if args.grad else "forward",
                    "discretization": "exact zero-order hold" if args.zoh else "delta B",
                    "inputs": "per-direction u, delta, B, C" if args.dirs else "shared",
+                   "chunks": "library's choice" if args.chunks in (None, 0) else args.chunks,
                    "launch": "one by one" if args.eager else "one HIP graph of the timed steps"},
         "hbm_GBps": round(hbm_gbs, 1),
         "kernel_ms": round(kern_avg_s * 1e3, 5),

@@ -123,6 +123,36 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    int delta_softplus, void* y, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/*
+ * vim_scan_bidir with the sequence cut into `chunks` pieces that run in
+ * parallel: the carry combine of a chunked scan. The inferensys glossary
+ * "Vision Mamba (Vim)" (item "Parallel Scan Algorithm") and the guide's
+ * "Production Engineering" section ("1. Compiling Fused CUDA Kernels") name a
+ * parallel associative scan for the recurrence; since
+ * h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t is linear in h, a run of
+ * steps acts on the incoming state as h -> P h + h_0 with
+ * P = prod_t exp(delta_t A) = exp(A sum_t delta_t) and h_0 its end state
+ * from zero, and these pairs compose associatively:
+ * (P1, h1) then (P2, h2) = (P1 P2, P2 h1 + h2). Each chunk first computes
+ * the pairs of the tokens before it (forward) and after it (backward),
+ * combines them into the states the two directions carry into the chunk,
+ * and then scans its own tokens from those states.
+ *   chunks         0: the library's choice (what vim_scan_bidir does: chunks
+ *                  only when batch and dim give under 2 waves per SIMD);
+ *                  1: one chunk; k >= 2: k chunks of whole 32-token tiles
+ *                  (at most one per tile). Only VS_FLAG_SOFTPLUS may be set.
+ *   everything else as for vim_scan_bidir (same workspace). The result is
+ *   the same function of the inputs for every chunk count, up to fp32
+ *   rounding of the carried states.
+ * Returns VS_ERR_UNSUPPORTED for chunks > 1 with VS_FLAG_ZOH, VS_ERR_SHAPE
+ * for chunks < 0.
+ */
+int vim_scan_bidir_chunked(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                           const void* u, const void* delta, const void* z, const void* B,
+                           const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                           int delta_softplus, int chunks, void* y, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Largest batch*dim*seqlen that vim_scan_bidir_noalloc takes for bf16
  * activations: its library-owned merge buffer holds this many fp32 values
  * (128 MiB per GPU). fp32 activations need no buffer (y holds the partial

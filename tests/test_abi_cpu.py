@@ -293,3 +293,19 @@ def test_noalloc_refuses_sizes_beyond_its_buffer(nat):
     rc = f(2, 8, 16, 33, nat.VS_BF16, None, far(1), far(2), far(3), far(4), far(5), far(6),
            far(7), 1, far(8), None)
     assert rc == -1
+
+
+def test_chunked_refuses_what_it_does_not_chunk(nat):
+    """vim_scan_bidir_chunked: a negative chunk count is a shape error, and
+    chunks with the exact hold are not supported; both before any HIP
+    call."""
+    f = nat.lib.vim_scan_bidir_chunked
+    args = [2, 8, 16, 333, nat.VS_BF16, far(0), far(1), far(2), far(3), far(4), far(5), far(6),
+            far(7)]
+    rc = f(*args, 1, -1, far(8), far(9), 1 << 40, None)
+    assert rc == -2
+    rc = f(*args, 3, 2, far(8), far(9), 1 << 40, None)           # VS_FLAG_SOFTPLUS | VS_FLAG_ZOH
+    assert rc == -6
+    assert b"chunks" in nat.lib.vs_last_error()
+    rc = f(*args, 1, 2, far(8), None, 0, None)                   # bf16 needs the workspace
+    assert rc == -8

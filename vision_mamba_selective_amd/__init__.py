@@ -7,7 +7,7 @@ The binding is imported lazily so that the generator can be used without the
 library.
 """
 
-__all__ = ["vim_scan_bidir", "vim_scan_bidir_noalloc", "vim_scan_bidir_dirs", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
+__all__ = ["vim_scan_bidir", "vim_scan_bidir_noalloc", "vim_scan_bidir_chunked", "vim_scan_bidir_dirs", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
            "vmamba_cross_scan4", "s6_scan_1d", "workspace_bytes", "vim_x_proj", "vim_dt_proj",
            "vim_out_proj"]
 

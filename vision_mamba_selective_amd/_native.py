@@ -26,6 +26,8 @@ SIGNATURES = {
     "vs_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I]),
     "vim_scan_bidir": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                             _P, _P, _SZ, _P]),
+    "vim_scan_bidir_chunked": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _I, _I, _P, _P, _SZ, _P]),
     "vim_scan_bidir_noalloc": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _I, _P, _P]),
     "vim_scan_bidir_dirs": (_I, [_I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,

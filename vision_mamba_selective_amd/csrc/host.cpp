@@ -76,6 +76,8 @@ int validate(const Call& c) {
     if (c.L > kMaxElems || c.dim > kMaxElems)
         return fail(VS_ERR_SHAPE, "sequence length or dim too large");
     if (c.chunks < 0) return fail(VS_ERR_SHAPE, "the chunk count must be >= 0");
+    if (c.chunks > 1 && (c.mode != kModeVim || c.conv || c.zoh || c.per_dir))
+        return fail(VS_ERR_UNSUPPORTED, "chunks: the plain Vim scan only (no ZOH)");
     // kernels address every tensor with 32-bit byte offsets (fp32 partial
     // sums included), so each tensor must stay below 4 GiB. Every factor is
     // bounded above by now, and the products are formed only once they are

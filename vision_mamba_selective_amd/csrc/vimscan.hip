@@ -87,6 +87,7 @@ struct ScanArgs {
     int softplus;
     int reverse;        // 1-D mode only
     int nblk;           // ceil(L / 16)
+    int nchunk;         // chunked Vim scan: chunks per sequence (grid.y = batch * nchunk)
 };
 
 // The kernels' per-block steps are lambdas over register arrays (token
@@ -249,10 +250,30 @@ struct Unroll<0> {
 // sums are read only after it. Vim finishes a token by gating and storing
 // y; the cross-scan stores the pair's sum, and after the loop the workgroup
 // adds its two pairs' sums, gates and stores y.
+//
+// CHUNK (Vim with shared inputs): the sequence is cut into a.nchunk chunks of
+// whole 32-token tiles and each workgroup scans one chunk c, tokens
+// [s_c, e_c), in both directions, as above over that sub-sequence. Its rows
+// start from the states the directions carry into the chunk: the forward
+// direction's state after tokens [0, s_c), the backward direction's after
+// tokens [e_c, L) taken from L-1 down. A first phase computes them in the
+// workgroup: a row scans a piece of that prefix or suffix from h = 0 (no
+// read-out) and keeps the piece's aggregate (P_n = prod_t exp(delta_t A_n) =
+// exp(A_n sum_t delta_t), h_n = its end state from 0). Aggregates compose
+// associatively in scan order, (P1, h1) o (P2, h2) = (P1 P2, P2 h1 + h2);
+// a prefix or suffix split over the channel's two rows is combined across
+// them with one lane swizzle. The channel's rows take:
+//   middle chunk   : row 0 the prefix (forward), row 1 the suffix (backward);
+//   first chunk    : the suffix, split: row 0 the part next to L (scanned
+//                    first), row 1 the rest, which then combines both;
+//   last chunk     : the prefix, split: row 1 the part from token 0, row 0
+//                    the rest, which then combines both.
 template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false,
-          bool ZOH = false>
+          bool ZOH = false, bool CHUNK = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
+    static_assert(!CHUNK || (MODE == kModeVim && !CONV && !CKPT && !ZOH),
+                  "chunks: the plain Vim scan only");
     // CKPT (the gradient's forward pass): store every row's state at each
     // block start and, in place of y, the merged ungated sum in the partial
     // buffer (fp32)
@@ -294,12 +315,23 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     }
     uint32_t cg, bb;
     xcd_block(cg, bb);
-    const int64_t b = bb;
+    // grid.y enumerates (batch, chunk), chunk fastest
+    const int nchunk = CHUNK ? a.nchunk : 1;
+    const int chunk = CHUNK ? static_cast<int>(bb % static_cast<uint32_t>(nchunk)) : 0;
+    const int64_t b = CHUNK ? bb / static_cast<uint32_t>(nchunk) : bb;
     const int64_t d0 = static_cast<int64_t>(cg) * kChPerWg + ch;
     const bool active = d0 < a.dim;
     const int64_t d = active ? d0 : 0;
-    const int L = static_cast<int>(a.L);
-    const int nblk = a.nblk;
+    const int Lseq = static_cast<int>(a.L);
+    // chunk c: tiles [c T / K, (c + 1) T / K) of the T = ceil(L / 32) tiles
+    const int ntile_seq = (Lseq + kPairTok - 1) / kPairTok;
+    auto chunk_start = [&](int k) {
+        const int t = static_cast<int>(static_cast<int64_t>(ntile_seq) * k / nchunk) * kPairTok;
+        return t < Lseq ? t : Lseq;
+    };
+    const int tok0 = CHUNK ? chunk_start(chunk) : 0;           // this workgroup's first token
+    const int L = CHUNK ? chunk_start(chunk + 1) - tok0 : Lseq; // and its token count
+    const int nblk = CHUNK ? (L + kBlockTok - 1) / kBlockTok : a.nblk;
     const bool rev = MODE == kMode1D ? a.reverse != 0 : (dir & 1) != 0;
     const int pside = dir & 1;                // position within the pair
 
@@ -310,6 +342,14 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const float rA = ZOH ? 1.f / An : 0.f;    // A = 0 only ever takes the series below
     const float Dk = (active && a.Dskip) ? a.Dskip[prow] : 0.f;
     const float bias = (active && a.dt_bias) ? a.dt_bias[prow] : 0.f;
+    // the other direction's A and dt_bias (a chunked row may scan a piece of
+    // the other direction's prefix or suffix first)
+    float A2_other = 0.f, bias_other = 0.f;
+    if (CHUNK && active) {
+        const int64_t orow = (1 - dir) * a.dim + d;
+        A2_other = n < a.dstate ? a.A[orow * a.dstate + n] * kLog2e : 0.f;
+        bias_other = a.dt_bias ? a.dt_bias[orow] : 0.f;
+    }
     // Vim front end: each branch's u = silu(b + w0 x[q-1] + w1 x[q] + w2 x[q+1])
     // over its own sequence order q, with zeros past the ends ("1. Forward
     // Branch", "2. Backward Branch (Reverse sequence)"). In token order the
@@ -395,75 +435,110 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     uint32_t cselx[kCpt], csely[kCpt];
     bool cok[kCpt];             // the chunk's state row is < dstate
     int cdst[kCpt];             // tile_mem index of the chunk in buffer 0
+    int ctok0[kCpt], clen[kCpt];    // the side's token range (uniform per wave)
+    // A side s reads tokens [sd_tok0[s], sd_tok0[s] + sd_len[s]) in token
+    // order, or from the top down when sd_rev[s]; with_c = false stages B only.
+    auto stage_setup = [&](const int (&sd_tok0)[kSides], const int (&sd_len)[kSides],
+                           const bool (&sd_rev)[kSides], bool with_c) VS_INLINE {
 #pragma unroll
-    for (int j = 0; j < kCpt; ++j) {
-        const int c0 = tid + j * kThreads;
-        cin[j] = kChunks % kThreads == 0 || __builtin_amdgcn_readfirstlane(c0 < kChunks ? 1 : 0) != 0;
-        const int c = c0 < kChunks ? c0 : 0;
-        const int row = c / kCpr, k = c % kCpr;
-        const int q = row / kRowLanes, srow = row % kRowLanes;
-        const int side = q >> 1;
-        const bool ok_row = srow < a.dstate;
-        const int64_t dsel = MODE == kModeCross4 ? side : (MODE == kModeVim && a.bc_per_dir ? side : 0);
-        const bool isC = __builtin_amdgcn_readfirstlane(q & 1) != 0;
-        csrc[j] = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<char*>(isC ? Cb : Bb) + static_cast<size_t>(b) * bc_batch_el * kEs, 0,
-            static_cast<int>(bc_batch_el * kEs), 0x00020000);
-        crow[j] = static_cast<uint32_t>((dsel * a.dstate + (ok_row ? srow : 0)) * a.L);
-        ccol[j] = k * kTpc;
-        const bool rv = MODE == kModeVim ? side == 1 : (MODE == kMode1D ? a.reverse != 0 : false);
-        crev[j] = MODE != kModeCross4 && __builtin_amdgcn_readfirstlane(rv ? 1 : 0) != 0;
-        cok[j] = ok_row;
-        cselx[j] = !ok_row ? kSelZero : (rv ? kSelRevX : kSelFwdX);
-        csely[j] = !ok_row ? kSelZero : (rv ? kSelRevY : kSelFwdY);
-        cdst[j] = ((side * 2 + (q & 1)) * kRowLanes + srow) * kPairPad + k * kTpc;
+        for (int j = 0; j < kCpt; ++j) {
+            const int c0 = tid + j * kThreads;
+            const int c = c0 < kChunks ? c0 : 0;
+            const int row = c / kCpr, k = c % kCpr;
+            const int q = row / kRowLanes, srow = row % kRowLanes;
+            const int side = q >> 1;
+            const bool ok_row = srow < a.dstate;
+            const int64_t dsel = MODE == kModeCross4 ? side : (MODE == kModeVim && a.bc_per_dir ? side : 0);
+            const bool isC = __builtin_amdgcn_readfirstlane(q & 1) != 0;
+            cin[j] = (kChunks % kThreads == 0 || __builtin_amdgcn_readfirstlane(c0 < kChunks ? 1 : 0) != 0) &&
+                     (with_c || !isC);
+            csrc[j] = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<char*>(isC ? Cb : Bb) + static_cast<size_t>(b) * bc_batch_el * kEs, 0,
+                static_cast<int>(bc_batch_el * kEs), 0x00020000);
+            crow[j] = static_cast<uint32_t>((dsel * a.dstate + (ok_row ? srow : 0)) * a.L);
+            ccol[j] = k * kTpc;
+            const bool rv = sd_rev[side];
+            crev[j] = MODE != kModeCross4 && __builtin_amdgcn_readfirstlane(rv ? 1 : 0) != 0;
+            ctok0[j] = sd_tok0[side];
+            clen[j] = sd_len[side];
+            cok[j] = ok_row;
+            cselx[j] = !ok_row ? kSelZero : (rv ? kSelRevX : kSelFwdX);
+            csely[j] = !ok_row ? kSelZero : (rv ? kSelRevY : kSelFwdY);
+            cdst[j] = ((side * 2 + (q & 1)) * kRowLanes + srow) * kPairPad + k * kTpc;
+        }
+    };
+    // The tile `pair` of chunk j's side, entry by entry and clamped into the
+    // side's range: entry i of the chunk in memory order holds scan step
+    // t0 + i (t0 + kTpc - 1 - i when reversed); steps past the range repeat
+    // its last step.
+    auto stage_entries = [&](int pair, int j) VS_INLINE {
+        const int t0 = pair * kPairTok + ccol[j];
+        uint32_t e[kTpc];
+#pragma unroll
+        for (int i = 0; i < kTpc; ++i) {
+            const int t = t0 + (crev[j] ? kTpc - 1 - i : i);
+            const int tc = t < clen[j] ? t : clen[j] - 1;
+            const int tok = ctok0[j] + (crev[j] ? clen[j] - 1 - tc : tc);
+            const int off = static_cast<int>((crow[j] + static_cast<uint32_t>(tok)) * kEs);
+            e[i] = sizeof(T) == 2 ? __builtin_amdgcn_raw_buffer_load_b16(csrc[j], off, 0, 0)
+                                  : __builtin_amdgcn_raw_buffer_load_b32(csrc[j], off, 0, 0);
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = sizeof(T) == 2 ? (e[2 * i] | (e[2 * i + 1] << 16)) : e[i];
+            // materialise here: packing at the use inside the loop would
+            // have to wait for every load then in flight
+            asm volatile("" : "+v"(w[i]));
+        }
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+    {
+        int sd_tok0[kSides], sd_len[kSides];
+        bool sd_rev[kSides];
+#pragma unroll
+        for (int sd = 0; sd < kSides; ++sd) {
+            sd_tok0[sd] = tok0;
+            sd_len[sd] = L;
+            sd_rev[sd] = MODE == kModeVim ? sd == 1 : (MODE == kMode1D ? a.reverse != 0 : false);
+        }
+        stage_setup(sd_tok0, sd_len, sd_rev, true);
     }
     const int ntile = (L + kPairTok - 1) / kPairTok;
     const bool tail_part = ntile * kPairTok > L;                // uniform
     uint4 tail_raw[kCpt];
-    if (tail_part) {
-        const int pair = ntile - 1;
+    // the scan's last tile, when the sequence does not fill it, is read once
+    // before the loop (nothing else in flight then) and kept in registers
+    auto load_tail = [&]() VS_INLINE {
+        if (tail_part) {
 #pragma unroll
-        for (int j = 0; j < kCpt; ++j) {
-            if (!cin[j]) continue;
-            const int t0 = pair * kPairTok + ccol[j];
-            // entry i of the chunk in memory order holds token t0 + i
-            // (t0 + kTpc - 1 - i when reversed); padding tokens repeat L-1
-            uint32_t e[kTpc];
-#pragma unroll
-            for (int i = 0; i < kTpc; ++i) {
-                const int t = t0 + (crev[j] ? kTpc - 1 - i : i);
-                const int tc = t < L ? t : L - 1;
-                const int off = static_cast<int>((crow[j] + static_cast<uint32_t>(crev[j] ? L - 1 - tc : tc)) * kEs);
-                e[i] = sizeof(T) == 2 ? __builtin_amdgcn_raw_buffer_load_b16(csrc[j], off, 0, 0)
-                                      : __builtin_amdgcn_raw_buffer_load_b32(csrc[j], off, 0, 0);
-            }
-            uint32_t w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                w[i] = sizeof(T) == 2 ? (e[2 * i] | (e[2 * i + 1] << 16)) : e[i];
-                // materialise here: packing at the use inside the loop would
-                // have to wait for every load then in flight
-                asm volatile("" : "+v"(w[i]));
-            }
-            tail_raw[j] = make_uint4(w[0], w[1], w[2], w[3]);
+            for (int j = 0; j < kCpt; ++j)
+                if (cin[j]) tail_raw[j] = stage_entries(ntile - 1, j);
         }
-    }
-    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) VS_INLINE {
-        const bool whole = (pair + 1) * kPairTok <= L;      // uniform
+    };
+    // whole tiles with one 16-byte load per chunk; a tile the side's range
+    // does not fill comes from tail_raw (in_loop_tail = false) or is read
+    // entry by entry here
+    auto stage_load_any = [&](int pair, uint4 (&raw)[kCpt], bool in_loop_tail) VS_INLINE {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
             if (!cin[j]) continue;
             const int t0 = pair * kPairTok + ccol[j];
+            const bool whole = (pair + 1) * kPairTok <= clen[j];      // uniform per wave
             if (whole) {
-                const uint32_t first = crev[j] ? static_cast<uint32_t>(L - kTpc - t0) : static_cast<uint32_t>(t0);
+                const uint32_t first = static_cast<uint32_t>(ctok0[j]) +
+                                       (crev[j] ? static_cast<uint32_t>(clen[j] - kTpc - t0)
+                                                : static_cast<uint32_t>(t0));
                 raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                        csrc[j], static_cast<int>((crow[j] + first) * kEs), 0, 0));
+            } else if (in_loop_tail) {
+                raw[j] = stage_entries(pair, j);
             } else {
                 raw[j] = tail_raw[j];
             }
         }
     };
+    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) VS_INLINE { stage_load_any(pair, raw, false); };
     auto stage_store = [&](int buf, const uint4 (&raw)[kCpt]) VS_INLINE {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
@@ -505,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
         const int tc = t < L ? t : L - 1;
-        return rev ? L - 1 - tc : tc;
+        return tok0 + (rev ? L - 1 - tc : tc);
     };
 
     // ---- this lane's token of a block; unconditional loads on a valid
@@ -521,7 +596,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         k.u = act_row(ub, u_row, p);
         if (CONV) {   // the neighbours (clamped; masked where they fall outside)
             k.ul = act_row(ub, u_row, p > 0 ? p - 1 : 0);
-            k.ur = act_row(ub, u_row, p < L - 1 ? p + 1 : L - 1);
+            k.ur = act_row(ub, u_row, p < Lseq - 1 ? p + 1 : Lseq - 1);
         }
         k.dl = act_row(db, dl_row, p);
         // z is needed only by the visit that finishes the token; other
@@ -534,23 +609,166 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 
     const int npair = (nblk + kBpt - 1) / kBpt;
     uint4 sr[kCpt];
-    stage_load(0, sr);
-    stage_store(0, sr);
     // token data rotates through kTokAhead + 1 register sets, so that the
     // loads of kTokAhead blocks are in flight while one block is computed
     // (deeper prefetch measured no faster)
     constexpr int kRing = kTokAhead + 1;
     static_assert(kRing % kBpt == 0, "a loop trip covers whole tiles");
     Tok tk[kRing];
+    auto wg_barrier = [&]() VS_INLINE {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+
+    float h = 0.f;
+    // ---- chunks: the states the two directions carry into this chunk
+    if constexpr (CHUNK) if (nchunk > 1) {
+        const bool pre = chunk > 0, suf = chunk < nchunk - 1;          // uniform
+        const int e_tok = tok0 + L;
+        // side s (row parity) scans tokens [pa_s, pa_s + pl_s) in direction
+        // pd_s (1: from the top down)
+        int pa0, pl0, pd0, pa1, pl1, pd1;
+        const bool split = !(pre && suf);
+        if (!split) {
+            pa0 = 0; pl0 = tok0; pd0 = 0;                      // the prefix, forward
+            pa1 = e_tok; pl1 = Lseq - e_tok; pd1 = 1;          // the suffix, backward
+        } else {
+            // one job [ja, jb) in direction jd, split in two pieces: the near
+            // one is scanned first, the far one (a whole number of tiles)
+            // after it
+            const int ja = pre ? 0 : e_tok, jb = pre ? tok0 : Lseq, jd = pre ? 0 : 1;
+            const int jl = jb - ja;
+            const int far_len = ((jl + kPairTok - 1) / kPairTok / 2) * kPairTok;
+            const int near_len = jl - far_len;
+            const int near_a = jd == 0 ? ja : jb - near_len;
+            const int far_a = jd == 0 ? ja + near_len : ja;
+            // the far piece goes to the row of direction jd, which combines
+            // both pieces into its own carry; the other row starts the chunk
+            // at a sequence end, from zero
+            pa0 = jd == 0 ? far_a : near_a;
+            pl0 = jd == 0 ? far_len : near_len;
+            pa1 = jd == 0 ? near_a : far_a;
+            pl1 = jd == 0 ? near_len : far_len;
+            pd0 = pd1 = jd;
+        }
+        const int mpa = pside ? pa1 : pa0, mpl = pside ? pl1 : pl0;
+        const int mlen = mpl > 0 ? mpl : 1;             // an empty piece reads a valid token
+        const bool mrev = (pside ? pd1 : pd0) != 0;
+        const bool own_dir = (pside ? pd1 : pd0) == dir;
+        const float A2a = own_dir ? A2 : A2_other;
+        const float bias_a = own_dir ? bias : bias_other;
+        {
+            const int sd_tok0[kSides] = {pa0, pa1};
+            const int sd_len[kSides] = {pl0 > 0 ? pl0 : 1, pl1 > 0 ? pl1 : 1};
+            const bool sd_rev[kSides] = {pd0 != 0, pd1 != 0};
+            stage_setup(sd_tok0, sd_len, sd_rev, false);
+        }
+        const int lmax = pl0 > pl1 ? pl0 : pl1;
+        const int nblk_a = (lmax + kBlockTok - 1) / kBlockTok;
+        const int npair_a = (nblk_a + kBpt - 1) / kBpt;
+        auto tok_load_a = [&](int blk, Tok& k) VS_INLINE {
+            const int t = blk * kBlockTok + n;
+            const int tc = t < mlen ? t : mlen - 1;
+            const int p = mpa + (mrev ? mlen - 1 - tc : tc);
+            k.p = p;
+            k.u = act_row(ub, u_row, p);
+            k.dl = act_row(db, dl_row, p);
+        };
+        stage_load_any(0, sr, true);
+        stage_store(0, sr);
+        Unroll<kTokAhead>::run([&](auto ic) {
+            constexpr int k = decltype(ic)::value;
+            tok_load_a(k < nblk_a ? k : nblk_a - 1, tk[k]);
+        });
+        wg_barrier();
+        float sdl = 0.f;          // this lane's share of the piece's sum of delta
+        auto step_a = [&](const int blk, Tok& cur, Tok& nxt) VS_INLINE {
+            const int buf = (blk / kBpt) & 1;
+            const int half = blk % kBpt;
+            if (half == 0) {
+                const int pair = blk / kBpt;
+                stage_load_any(pair + 1 < npair_a ? pair + 1 : pair, sr, true);
+            }
+            tok_load_a(blk + kTokAhead < nblk_a ? blk + kTokAhead : nblk_a - 1, nxt);
+            const bool ok = active && blk * kBlockTok + n < mpl;
+            const float cu = from_raw<T>(cur.u);
+            const float x = from_raw<T>(cur.dl) + bias_a;
+            const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
+            const float du = dlt * cu;
+            sdl += dlt;
+            const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][pside][0][n][half * kBlockTok]);
+            float Bv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 bq = Bt[q];
+                Bv[4 * q] = bq.x; Bv[4 * q + 1] = bq.y; Bv[4 * q + 2] = bq.z; Bv[4 * q + 3] = bq.w;
+            }
+            Unroll<16>::run([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                const float e = __builtin_amdgcn_exp2f(row_bcast<i>(dlt) * A2a);
+                h = fmaf(e, h, row_bcast<i>(du) * Bv[i]);
+            });
+            // with no read-out, nothing else ties the unrolled steps
+            // together: left free, the scheduler hoists the exps of later
+            // blocks and the kernel needs 246 VGPRs (2 waves per SIMD)
+            // instead of 81
+            asm volatile("" : "+v"(h));
+            if (half == kBpt - 1) {
+                stage_store(buf ^ 1, sr);
+                wg_barrier();
+            }
+        };
+        int blk = 0;
+        for (; blk + kTokAhead < nblk_a; blk += kRing) {
+            Unroll<kRing>::run([&](auto ic) {
+                constexpr int k = decltype(ic)::value;
+                step_a(blk + k, tk[k], tk[(k + kTokAhead) % kRing]);
+            });
+        }
+        Unroll<kTokAhead>::run([&](auto ic) {
+            constexpr int k = decltype(ic)::value;
+            if (blk + k < nblk_a) step_a(blk + k, tk[k], tk[(k + kTokAhead) % kRing]);
+        });
+        // every wave is past its last read of the tile buffers before the
+        // chunk's own scan stages into them
+        wg_barrier();
+        if (split) {
+            // the far row composes the near piece's aggregate with its own:
+            // carry = P_far h_near + h_far, P_far = exp(A sum(delta)) over
+            // the far piece. The near piece is the other row of the channel,
+            // 16 lanes away in the same 32-lane half of the wave.
+            float S = sdl;
+            S += dpp<0x128>(S);                                  // row_ror:8
+            S += dpp<0x124>(S);                                  // row_ror:4
+            S += dpp<0x122>(S);                                  // row_ror:2
+            S += dpp<0x121>(S);                                  // row_ror:1
+            const float h_other = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(h), 0x401f));
+            const bool far_row = own_dir;                        // the row of the job's direction
+            h = far_row ? fmaf(__builtin_amdgcn_exp2f(A2a * S), h_other, h) : 0.f;
+        }
+        {
+            int sd_tok0[kSides], sd_len[kSides];
+            bool sd_rev[kSides];
+#pragma unroll
+            for (int sd = 0; sd < kSides; ++sd) {
+                sd_tok0[sd] = tok0;
+                sd_len[sd] = L;
+                sd_rev[sd] = sd == 1;
+            }
+            stage_setup(sd_tok0, sd_len, sd_rev, true);
+        }
+    }
+
+    load_tail();
+    stage_load(0, sr);
+    stage_store(0, sr);
     Unroll<kTokAhead>::run([&](auto ic) {
         constexpr int k = decltype(ic)::value;
         tok_load(k < nblk ? k : nblk - 1, tk[k]);
     });
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    wg_barrier();
 
-    float h = 0.f;
     float* ck_row = nullptr;
     if (CKPT)
         ck_row = a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
@@ -587,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         float cu = from_raw<T>(cur.u);
         if (CONV) {
             const float xl = p > 0 ? from_raw<T>(cur.ul) : 0.f;
-            const float xr = p < L - 1 ? from_raw<T>(cur.ur) : 0.f;
+            const float xr = p < Lseq - 1 ? from_raw<T>(cur.ur) : 0.f;
             cu = silu_f(fmaf(cw_l, xl, fmaf(cw_c, cu, fmaf(cw_r, xr, cw_b))));
         }
         const float x = from_raw<T>(cur.dl) + bias;
@@ -1230,6 +1448,43 @@ using vs::Call;
 using vs::GradCall;
 using vs::fail;
 
+template <typename T>
+void launch_chunked(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a) {
+    constexpr int V = kModeVim;
+    if (c.z && c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, true, true, false, false, false, true>), grid, blk, 0, st, a);
+    else if (c.z)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, true, false, false, false, false, true>), grid, blk, 0, st, a);
+    else if (c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, false, true, false, false, false, true>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, V, false, false, false, false, false, true>), grid, blk, 0, st, a);
+}
+
+// Chunks per sequence for a plain Vim scan. Unchunked, the launch has
+// batch * ceil(dim / 8) workgroups of 4 waves; below 2 waves per SIMD (1,024
+// SIMDs) the chip is under-filled and the sequential length sets the time, so
+// the sequence is cut into chunks until the grid reaches about 3 waves per
+// SIMD, and into at most 3: each chunk first rescans its prefix or suffix
+// (measured: Vim-B 2048^2, 1.5 waves per SIMD unchunked, 0.766 ms, 2 chunks
+// 0.694 ms, 3 chunks 0.873 ms; Vim-Ti 224^2, 0.19 waves per SIMD, 11.1,
+// 11.7, 10.2 and 10.9 us per step for 1 to 4 chunks). Never more chunks
+// than 32-token tiles.
+int chunk_count(const Call& c) {
+    const int64_t ntile = (c.L + vs::kTileTok - 1) / vs::kTileTok;
+    int64_t k = c.chunks;
+    if (k == 0) {
+        const int64_t waves = c.batch * ((c.dim + 7) / 8) * 4;
+        const int64_t simds = vs::kNumCUs * 4;
+        k = waves >= 2 * simds ? 1 : (3 * simds) / waves;
+        k = k < 1 ? 1 : (k > 3 ? 3 : k);
+    }
+    // at most one chunk per tile, and grid.y = batch * chunks within 65535
+    const int64_t kmax = 65535 / c.batch;
+    k = k < ntile ? k : ntile;
+    return static_cast<int>(k < kmax ? k : kmax);
+}
+
 template <typename T, int MODE, bool CONV, bool ZOH>
 void launch_scan(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a) {
     if (c.z && c.softplus)
@@ -1244,7 +1499,7 @@ void launch_scan(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanA
 
 template <typename T, int MODE>
 int launch_t(const Call& c) {
-    ScanArgs a;
+    ScanArgs a{};
     a.u = c.u; a.delta = c.delta; a.z = c.z; a.B = c.B; a.C = c.C;
     a.A = c.A; a.Dskip = c.Dskip; a.dt_bias = c.dt_bias; a.y = c.y;
     a.conv_w = c.conv_w; a.conv_b = c.conv_b;
@@ -1284,7 +1539,15 @@ int launch_t(const Call& c) {
                            const_cast<T*>(static_cast<const T*>(a.deltaT)), c.H, c.W, rows);
     }
     if constexpr (MODE == kModeVim) {
-        if (c.conv_w) {
+        // the plain scan takes chunks when the grid under-fills the chip
+        const bool plain = !c.conv_w && !c.zoh && !c.per_dir;
+        const int nchunk = plain ? chunk_count(c) : 1;
+        if (nchunk > 1) {
+            ScanArgs ac = a;
+            ac.nchunk = nchunk;
+            const dim3 cgrid(grid.x, grid.y * static_cast<unsigned>(nchunk));
+            launch_chunked<T>(c, cgrid, blk, st, ac);
+        } else if (c.conv_w) {
             if (c.zoh) launch_scan<T, MODE, true, true>(c, grid, blk, st, a);
             else launch_scan<T, MODE, true, false>(c, grid, blk, st, a);
         } else if (c.zoh) {
@@ -1433,6 +1696,17 @@ int vim_scan_bidir(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    void* stream) {
     Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
            A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    return run(c);
+}
+
+int vim_scan_bidir_chunked(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                           const void* u, const void* delta, const void* z, const void* B,
+                           const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                           int delta_softplus, int chunks, void* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
+           A, Dskip, dt_bias, delta_softplus, y, workspace, workspace_bytes, stream};
+    c.chunks = chunks;
     return run(c);
 }
 

@@ -94,6 +94,34 @@ def vim_scan_bidir(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplu
     return y
 
 
+def vim_scan_bidir_chunked(u, delta, z, B, C, A, Dskip=None, dt_bias=None, chunks=0,
+                           delta_softplus=True, out=None, workspace=None):
+    """vim_scan_bidir with the sequence cut into `chunks` parallel pieces
+    joined by the associative carry combine (0: the library's choice)."""
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    y = torch.empty_like(u) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_BIDIR, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir_chunked(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                        _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                        _ptr(dt_bias), _flags(delta_softplus, False), int(chunks),
+                                        _ptr(y), _ptr(ws), ws_bytes, _stream(dev))
+    nat.check("vim_scan_bidir_chunked", rc)
+    return y
+
+
 def vim_scan_bidir_noalloc(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
                            zoh=False, out=None):
     """vim_scan_bidir without a workspace: the merge buffer is the library's
