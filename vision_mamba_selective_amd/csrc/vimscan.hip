@@ -387,6 +387,52 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto y_at = [&](int p) {
         return reinterpret_cast<T*>(yb + (rowoff + static_cast<uint32_t>(p)) * kEs);
     };
+    // Vim token addressing (every form but the conv front end): a wave's two
+    // channels are adjacent rows of [batch][dim][L], so one buffer descriptor
+    // per tensor covers the wave, and a lane's token of block blk is one byte
+    // offset ob0 + blk * ob_inc, never clamped: past either end of the
+    // sequence it falls in the wave's other row (a token no step uses) or
+    // outside the descriptor, where loads return 0. Loads that a block does
+    // not need (the gate and the partial sum before the token's second
+    // visit) take an out-of-range scalar offset and read nothing.
+    constexpr bool kRun = MODE == kModeVim && !CONV;
+    constexpr int kOob = 0x40000000;
+    const int64_t wave_d0 = static_cast<int64_t>(cg) * kChPerWg + 2 * wave;
+    const int64_t wave_left = a.dim - wave_d0;
+    const int64_t wave_nch = wave_left < 0 ? 0 : (wave_left > 2 ? 2 : wave_left);
+    const size_t wave_base = static_cast<size_t>((b * a.dim + (wave_nch > 0 ? wave_d0 : 0)) * a.L);
+    const uint32_t wave_el = static_cast<uint32_t>(wave_nch * a.L);
+    auto wave_rsrc = [&](const void* base, uint32_t es, uint32_t extra_el) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(static_cast<const char*>(base)) + wave_base * es, 0,
+            static_cast<int>((wave_el + extra_el) * es), 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t rs_u = wave_rsrc(a.u, kEs, a.u_dir_off);
+    const __amdgpu_buffer_rsrc_t rs_dl = wave_rsrc(a.delta, kEs, a.dl_dir_off);
+    const __amdgpu_buffer_rsrc_t rs_z = wave_rsrc(GATE ? a.z : a.u, kEs, 0u);
+    const __amdgpu_buffer_rsrc_t rs_y = wave_rsrc(CKPT ? a.u : a.y, kEs, 0u);
+    const __amdgpu_buffer_rsrc_t rs_p = wave_rsrc(a.partial, 4u, 0u);
+    // an inactive channel's lanes land past the wave's rows (no store ever
+    // uses them)
+    const int lane_rel = static_cast<int>((d0 - wave_d0) * a.L);
+    const int ob0 = (lane_rel + tok0 + (rev ? L - 1 - n : n)) * static_cast<int>(kEs);
+    const int ob_inc = (rev ? -kBlockTok : kBlockTok) * static_cast<int>(kEs);
+    const int ou_lane = rev ? static_cast<int>(a.u_dir_off * kEs) : 0;
+    const int od_lane = rev ? static_cast<int>(a.dl_dir_off * kEs) : 0;
+    auto rload = [&](__amdgpu_buffer_rsrc_t r, int off, int soff) VS_INLINE {
+        if constexpr (sizeof(T) == 2)
+            return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
+        else
+            return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0));
+    };
+    auto rstore = [&](__amdgpu_buffer_rsrc_t r, int off, float v) VS_INLINE {
+        if constexpr (sizeof(T) == 2)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)), r, off, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+    };
+    // byte offset of a token's fp32 partial sum from its activation offset
+    auto poff = [&](int ob) { return ob * static_cast<int>(4 / kEs); };
 
     // ---- B/C staging, one tile per kPairTok tokens. The tile's rows are
     // (side, B|C, state); a row's entries are 16-byte chunks (8
@@ -591,6 +637,15 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     using Raw = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
     struct Tok { Raw u, dl, z, ul, ur; int p; };
     auto tok_load = [&](int blk, Tok& k) VS_INLINE {
+        if constexpr (kRun) {
+            // p holds the token's byte offset within the wave's rows
+            const int ob = ob0 + blk * ob_inc;
+            k.p = ob;
+            k.u = static_cast<Raw>(rload(rs_u, ob + ou_lane, 0));
+            k.dl = static_cast<Raw>(rload(rs_dl, ob + od_lane, 0));
+            if (GATE) k.z = static_cast<Raw>(rload(rs_z, ob, blk >= Fstep ? 0 : kOob));
+            return;
+        }
         const int p = tok_pos(blk);
         k.p = p;
         k.u = act_row(ub, u_row, p);
@@ -789,7 +844,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // entry 0 of the row instead (unused) rather than branch. Issued
         // before the prefetch so that waiting for it does not wait for those.
         float part = 0.f;
-        if (MODE != kMode1D)
+        if (kRun)      // agent-coherent (sc1), as the atomic load below
+            part = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_p, poff(p), blk > Fstep ? 0 : kOob, 16));
+        else if (MODE != kMode1D)
             part = __hip_atomic_load(part_at(blk > Fstep ? p : 0), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
         // prefetch; near the end this reloads the last pair or block
@@ -849,20 +906,31 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const float gate = (GATE && MODE != kModeCross4) ? silu_f(from_raw<T>(cur.z)) : 1.f;
         // a token's second visit: Vim gates and stores y, the cross-scan
         // stores the pair's fp32 sum
-        auto finish = [&](float sum) {
-            if (MODE == kModeCross4 || CKPT) *part_at(p) = sum;
-            else st(y_at(p), 0, sum * gate);
+        auto finish = [&](float sum, int pp) {
+            if (kRun) {
+                if (CKPT) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rs_p, poff(pp), 0, 0);
+                else rstore(rs_y, pp, sum * gate);
+            } else if (MODE == kModeCross4 || CKPT) {
+                *part_at(pp) = sum;
+            } else {
+                st(y_at(pp), 0, sum * gate);
+            }
         };
 
         if (MODE == kMode1D) {
             if (ok) st(y_at(p), 0, yk * gate);
         } else if (blk < Fstep) {
-            if (ok) *part_at(p) = yk;
+            if (ok) {
+                if (kRun) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yk), rs_p, poff(p), 0, 0);
+                else *part_at(p) = yk;
+            }
         } else if (blk > Fstep) {
-            if (ok) finish(yk + part);
+            if (ok) finish(yk + part, p);
         } else {
             // step F: tokens finished by the other direction in an earlier
-            // step, or (forward row) shared with the backward row in this one
+            // step, or (forward row) shared with the backward row in this one.
+            // It addresses the token by its index (once per scan).
+            const int p = tok_pos(blk);
             const int t_self = blk * kBlockTok + n;
             const int blk_other = (L - 1 - t_self) / kBlockTok;
             const bool first = blk < blk_other || (blk == blk_other && pside == 0);
@@ -872,7 +940,13 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             if (ok && !first) {
                 const float other = __hip_atomic_load(part_at(p), __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT);
-                finish(yk + other);
+                if (kRun) {
+                    // finish through the element pointer as well
+                    if (CKPT) *part_at(p) = yk + other;
+                    else st(y_at(p), 0, (yk + other) * gate);
+                } else {
+                    finish(yk + other, p);
+                }
             }
         }
 
