@@ -125,6 +125,25 @@ __device__ __forceinline__ float dpp(float v) {
 // value of lane I of this 16-lane row, in every lane of the row (row_newbcast)
 template <int I>
 __device__ __forceinline__ float row_bcast(float v) { return dpp<0x150 + I>(v); }
+// acc + row_bcast<I>(v) * w as one v_fmac_f32_dpp. The compiler does not fold
+// a DPP move into fmac (whose accumulator is tied to its result), so the
+// instruction is written out, and the compiler does not see its DPP read: a
+// DPP source needs two wait states after its VALU write. With FIRST the asm
+// opens with s_nop 1, for the first of a chain of calls that read one source;
+// the later calls of the chain read the same value, written before the
+// first. tests/test_dpp_hazards.py checks the rule on every path of the
+// built code object.
+template <int I, bool FIRST>
+__device__ __forceinline__ float row_bcast_fmac(float acc, float v, float w) {
+    static_assert(I >= 0 && I < 16, "a lane of the row");
+    if constexpr (FIRST)
+        asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(v), "v"(w), "i"(I));
+    else
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+            : "+v"(acc) : "v"(v), "v"(w), "i"(I));
+    return acc;
+}
 
 // Transpose-reduce across the 16 lanes of a row: lane n holds c[i] = its
 // state's share of token i's read-out; on return lane j holds the sum over
@@ -1073,8 +1092,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //     CKPT), keeping h_t and e_t = exp(delta_t A_n) in registers;
 //   * the adjoint runs backwards over the 16 steps,
 //       lam_t = gs_t C_t + e_{t+1} lam_{t+1},  gs = dy * silu(z),
-//     with lam and e_{t+1} carried across blocks;
-//   * per step and state: q = lam h_{t-1} e_t, dA += q delta_t,
+//     carrying e_{t+1} lam_{t+1} from step to step and across blocks;
+//   * per step and state: q = (lam e_t) h_{t-1}, dA += q delta_t,
 //     dC_t = gs_t h_t, dB_t = lam_t delta_t u_t; the sums over states
 //     R_w = sum_n lam B_t and R_v = sum_n q A_n are row transpose
 //     reductions (lane j ends with step j's sums), giving
@@ -1280,7 +1299,7 @@ void rowgrad_kernel(const GradArgs a) {
     // go to pdu, pdd, and dz is written there), blocks below F the second
     // (partial added, du and ddelta written); block F mixes both.
     constexpr int kFirst = 0, kMixed = 1, kSecond = 2;
-    float lam = 0.f, e_carry = 0.f, dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
+    float lamE = 0.f, dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
     auto step = [&](auto phase, const int blk, Tok& cur, Tok& nxt) VS_INLINE {
         constexpr int PH = decltype(phase)::value;
         const int buf = blk & 1;
@@ -1323,8 +1342,8 @@ void rowgrad_kernel(const GradArgs a) {
         // second copies of the broadcast sources, opaque to the compiler, so
         // that each broadcast has one use and folds into it as a DPP operand
         // (one shared broadcast would cost a separate v_mov_b32_dpp)
-        float dlt2 = dlt, du2 = du_, gs2 = gs;
-        asm volatile("" : "+v"(dlt2), "+v"(du2), "+v"(gs2));
+        float du2 = du_, gs2 = gs;
+        asm volatile("" : "+v"(du2), "+v"(gs2));
 
         const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][dir][0][n][0]);
         const float4* Ct = reinterpret_cast<const float4*>(&tile[buf][dir][1][n][0]);
@@ -1347,20 +1366,21 @@ void rowgrad_kernel(const GradArgs a) {
                 hs[i] = h;
             });
         }
-        // adjoint, backwards over the block's steps
+        // adjoint, backwards over the block's steps: lam_i = e_{i+1} lam_{i+1}
+        // + gs_i C_i, where lamE = e_{i+1} lam_{i+1} comes from the step
+        // before (zero past the sequence's end)
         float wv[16], vv[16], sbc[16];
         Unroll<16>::run([&](auto ic) {
             constexpr int i = 15 - decltype(ic)::value;
-            const float e_next = i < 15 ? es[i < 15 ? i + 1 : 15] : e_carry;
-            lam = fmaf(e_next, lam, row_bcast<i>(gs) * Cv[i]);
+            const float lam = row_bcast_fmac<i, i == 15>(lamE, gs, Cv[i]);
+            lamE = lam * es[i];
             const float hprev = i > 0 ? hs[i > 0 ? i - 1 : 0] : h_in;
-            const float q = lam * hprev * es[i];
-            dA_acc = fmaf(row_bcast<i>(dlt2), q, dA_acc);
+            const float q = lamE * hprev;
+            dA_acc = row_bcast_fmac<i, i == 15>(dA_acc, dlt, q);
             wv[i] = lam * Bv[i];
             vv[i] = q * An;
             sbc[i] = swap32_sum(row_bcast<i>(du2) * lam, row_bcast<i>(gs2) * hs[i]);
         });
-        e_carry = es[0];
         const float Rw = row_transpose_sum(wv, lane);
         const float Rv = row_transpose_sum(vv, lane);
         const float du_tok = fmaf(dlt, Rw, gs * Dk);
