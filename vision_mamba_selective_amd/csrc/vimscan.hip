@@ -1195,15 +1195,17 @@ void rowgrad_kernel(const GradArgs a) {
         a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
 
     // ---- B/C staging (as rowscan_kernel: side 0 reads token t, side 1 L-1-t),
-    // by the first 256 threads: thread (sn, slot) moves state sn of step slot
+    // by the first 256 threads (whole waves; the other waves load nothing):
+    // thread (sn, slot) moves state sn of step slot
     constexpr int kStage = 4;
-    const bool stager = tid < kThreads;
+    const bool stager = __builtin_amdgcn_readfirstlane(tid >> 6) < kThreads / kWaveLanes;
     const int sn = (tid >> 4) & (kRowLanes - 1), slot = tid & 15;
     const bool sn_ok = sn < a.dstate;
     const uint32_t bc_row = static_cast<uint32_t>((b * a.dstate + (sn_ok ? sn : 0)) * a.L);
     const char* __restrict__ Bb = static_cast<const char*>(a.B);
     const char* __restrict__ Cb = static_cast<const char*>(a.C);
     auto stage_load = [&](int blk, uint32_t (&sr)[kStage]) VS_INLINE {
+        if (!stager) return;
         const int t = blk * kBlockTok + slot;
         const int tc = t < L ? t : L - 1;
 #pragma unroll
