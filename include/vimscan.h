@@ -243,10 +243,9 @@ int vim_scan_bidir_conv(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
  *                  over batch rows); returned even when Dskip / dt_bias are
  *                  NULL (the gradient at 0)
  *   workspace      at least vs_workspace_bytes(VS_OP_VIM_GRAD, ...) bytes
- * Every output is overwritten. du, ddelta, dz, dB and dC are the same bit
- * for bit on every call (dB and dC are summed in a fixed order); dA, dD and
- * ddt_bias are sums of fp32 atomic additions, so their last bits may differ
- * between calls. No output may overlap an input, another output or the
+ * Every output is overwritten, and is the same bit for bit on every call:
+ * each per-token output has one writer, and the sums over channels and
+ * batch rows are taken in a fixed order (no atomics). No output may overlap an input, another output or the
  * workspace (VS_ERR_ALIAS). Sequences longer than 2^26 tokens return
  * VS_ERR_UNSUPPORTED.
  */

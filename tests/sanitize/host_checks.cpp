@@ -101,9 +101,13 @@ void workspace_sizes() {
     CHECK(vs::scan_ws_bytes(VS_OP_CROSS4, 65535, 1 << 20, 1 << 20, VS_F32) == 0);
     CHECK(vs::scan_ws_bytes(VS_OP_VIM_GRAD, kMax, 2, 2, VS_BF16) == 0);
     CHECK(vs::scan_ws_bytes(VS_OP_VIM_GRAD, 8, 768, 4097, VS_BF16) > size_t(8) * 768 * 4097 * 12);
-    size_t offs[5];
+    size_t offs[6];
     const size_t g = vs::grad_ws_bytes(1, 1, 1, offs);
-    CHECK(offs[0] == 0 && offs[4] < g && g % 256 == 0);
+    CHECK(offs[0] == 0 && offs[4] < offs[5] && offs[5] < g && g % 256 == 0);
+    // the per-batch parameter sums hold 2 x dim x (dstate + 2) floats per
+    // batch row for the largest dstate
+    const size_t g2 = vs::grad_ws_bytes(3, 5, 7, offs);
+    CHECK(g2 - offs[5] >= size_t(4) * 3 * 2 * 5 * (VS_MAX_DSTATE + 2));
 }
 
 void grad_validation() {

@@ -124,17 +124,16 @@ def test_grad_softplus_off(base):
     compare(got, ref, wl.dtype, "grad softplus off")
 
 
-def test_grad_per_token_outputs_are_repeatable():
-    """du, ddelta and dz have one writer per element, and dB and dC are summed
-    in a fixed order: identical bits across calls (dA, dD and ddt_bias are
-    summed with atomics and may differ in their last bits)."""
+def test_grad_outputs_are_repeatable():
+    """du, ddelta and dz have one writer per element, and dB, dC, dA, dD and
+    ddt_bias are summed in a fixed order: identical bits across calls."""
     wl = VIM_BF16.with_(batch=2, dim=16, seqlen=100)
     inp = wlm.make_inputs(wl)
     dy = upstream(inp, seed=4)
     say("case grad repeatable")
     a = run_grad(inp, dy)
     b = run_grad(inp, dy)
-    for k in PER_TOKEN + ("dB", "dC"):
+    for k in PER_TOKEN + SUMMED:
         assert torch.equal(a[k], b[k]), k
 
 

@@ -49,7 +49,7 @@ size_t scan_ws_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dty
     // are formed only for sizes under that
     if (!product_below(batch, dim, seqlen, kMaxElems)) return 0;
     if (op == VS_OP_VIM_GRAD) {
-        size_t offs[5];
+        size_t offs[6];
         return grad_ws_bytes(batch, dim, seqlen, offs);
     }
     // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
@@ -157,7 +157,7 @@ int grad_channels(int64_t batch, int64_t dim) {
 // workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
 // [du partials: fp32 E][ddelta partials: fp32 E][dB/dC chunks], each 256-byte
 // aligned. Sizes must have passed the 2^30-element checks.
-size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
+size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[6]) {
     const size_t elems = static_cast<size_t>(batch * dim * L);
     const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
     const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
@@ -171,6 +171,9 @@ size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]) {
     offs[2] = off; off += al(4 * elems);     // du partials
     offs[3] = off; off += al(4 * elems);     // ddelta partials
     offs[4] = off; off += al(4 * chunks);    // dB/dC chunks
+    // per batch row: dA [2][dim][dstate], dD [2][dim], ddt_bias [2][dim]
+    // (sized for the largest dstate)
+    offs[5] = off; off += al(4 * static_cast<size_t>(batch * 2 * dim * (VS_MAX_DSTATE + 2)));
     return off;
 }
 
@@ -201,7 +204,7 @@ int validate_grad(const GradCall& g) {
     const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
     for (const void* p : fps)
         if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
-    size_t offs[5];
+    size_t offs[6];
     const size_t need = grad_ws_bytes(g.batch, g.dim, g.L, offs);
     if (!g.ws || g.ws_bytes < need)
         return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");

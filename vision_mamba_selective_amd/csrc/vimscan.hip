@@ -1109,8 +1109,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //     stores its 1024 block sums (dB|dC x side x state x step) as one
 //     contiguous 4 KB chunk. grad_bc_reduce_kernel then sums the chunks over
 //     the workgroups in a fixed order, so no atomics are involved and dB and
-//     dC repeat bit for bit. dA, dD and dt_bias are summed per row and added
-//     once at the end with atomics.
+//     dC repeat bit for bit. dA, dD and dt_bias are summed per row, stored
+//     per batch row, and summed over the batch rows by the same kernel, in
+//     order, so they repeat bit for bit as well.
 using vs::kBcChunk;               // floats per workgroup and block: [dB|dC][side][n][step]
 
 struct GradArgs {
@@ -1121,7 +1122,7 @@ struct GradArgs {
     float *pdu, *pdd;       // fp32 partial sums of du and ddelta_raw
     void *du, *ddelta, *dz;
     float *bc_part;         // [batch][group][block][kBcChunk] dB/dC chunks
-    float *dA, *dD, *dbias;
+    float *pstat;           // per batch row: dA, dD, dt_bias sums (kernel-wide strides)
     int64_t dim, L;
     int dstate, nblk;
 };
@@ -1469,26 +1470,42 @@ void rowgrad_kernel(const GradArgs a) {
         tA = tB;
     }
 
-    // per-row sums: dA (lane n), dD and dt_bias (summed over the row's lanes)
-    if (n_ok) atomicAdd(&a.dA[prow * a.dstate + n], dA_acc);
+    // per-row sums: dA (lane n), dD and dt_bias (summed over the row's lanes),
+    // stored for this batch row; grad_bc_reduce_kernel sums the batch rows
+    float* const ps = a.pstat + static_cast<size_t>(b) * 2 * a.dim * (a.dstate + 2);
+    if (n_ok) ps[prow * a.dstate + n] = dA_acc;
     float sD = dD_acc, sb2 = dbias_acc;
     sD += dpp<0x4e>(sD); sb2 += dpp<0x4e>(sb2);              // quad_perm [2,3,0,1]
     sD += dpp<0xb1>(sD); sb2 += dpp<0xb1>(sb2);              // quad_perm [1,0,3,2]
     sD += dpp<0x114>(sD); sb2 += dpp<0x114>(sb2);            // row_shr:4 (lane 15: + lane 11)
     sD += dpp<0x118>(sD); sb2 += dpp<0x118>(sb2);            // row_shr:8 (lane 15: + lane 7)
     if (active && n == 15) {
-        atomicAdd(&a.dD[prow], sD);
-        atomicAdd(&a.dbias[prow], sb2);
+        ps[2 * a.dim * a.dstate + prow] = sD;
+        ps[2 * a.dim * (a.dstate + 1) + prow] = sb2;
     }
 }
 
 // dB and dC from the gradient kernel's chunks: the sum over the workgroups of
 // side 0 at step t = token t and side 1 at step t = token L-1-t. One thread
 // per (state, token) of a 16-token block; the workgroups are added in a fixed
-// order.
+// order. The workgroups past the nblk blocks of batch row 0 sum dA, dD and
+// dt_bias over the batch rows, in order, one thread per output.
 __global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
         const float* __restrict__ part, float* __restrict__ dB, float* __restrict__ dC, int64_t L,
-        int dstate, int nblk, int ngroups) {
+        int dstate, int nblk, int ngroups, const float* __restrict__ pstat, float* __restrict__ dA,
+        float* __restrict__ dD, float* __restrict__ dbias, int64_t dim, int batch) {
+    if (static_cast<int>(blockIdx.x) >= nblk) {
+        const int64_t np = 2 * dim * (dstate + 2);
+        const int64_t k = static_cast<int64_t>(blockIdx.x - nblk) * kThreads + threadIdx.x;
+        if (blockIdx.y != 0 || k >= np) return;
+        float sum = 0.f;
+        for (int b = 0; b < batch; ++b) sum += pstat[static_cast<size_t>(b) * np + k];
+        const int64_t na = 2 * dim * dstate;
+        if (k < na) dA[k] = sum;
+        else if (k < na + 2 * dim) dD[k - na] = sum;
+        else dbias[k - na - 2 * dim] = sum;
+        return;
+    }
     const int n = threadIdx.x >> 4, i = threadIdx.x & 15;
     const int64_t b = blockIdx.y;
     const int64_t tok = static_cast<int64_t>(blockIdx.x) * kBlockTok + i;
@@ -1509,12 +1526,6 @@ __global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
     const size_t o = static_cast<size_t>(b * dstate + n) * static_cast<size_t>(L) + static_cast<size_t>(tok);
     dB[o] = sB;
     dC[o] = sC;
-}
-
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-    for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * kThreads)
-        p[i] = 0.f;
 }
 
 // Transpose u and delta of every (batch, channel) from the row-major H x W
@@ -1697,7 +1708,7 @@ void launch_rowgrad(bool gate, bool softplus, dim3 grid, hipStream_t st, const G
 
 template <typename T>
 int launch_grad(const GradCall& g) {
-    size_t offs[5];
+    size_t offs[6];
     grad_ws_bytes(g.batch, g.dim, g.L, offs);
     char* ws = static_cast<char*>(g.ws);
     float* sbuf = reinterpret_cast<float*>(ws + offs[0]);
@@ -1722,15 +1733,7 @@ int launch_grad(const GradCall& g) {
         hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), fgrid, blk, 0, st, a);
     else
         hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), fgrid, blk, 0, st, a);
-    // 2. the atomically summed gradients start from zero
-    float* zs[] = {g.dA, g.dD, g.dbias};
-    const int64_t zn[] = {2 * g.dim * g.dstate, 2 * g.dim, 2 * g.dim};
-    for (int i = 0; i < 3; ++i) {
-        const int64_t nb = (zn[i] + kThreads - 1) / kThreads;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(nb < 4096 ? nb : 4096)), blk,
-                           0, st, zs[i], zn[i]);
-    }
-    // 3. reverse pass
+    // 2. reverse pass
     GradArgs r{};
     r.u = g.u; r.delta = g.delta; r.z = g.z; r.B = g.B; r.C = g.C; r.dy = g.dy;
     r.A = g.A; r.Dskip = g.Dskip; r.dt_bias = g.dt_bias;
@@ -1739,16 +1742,18 @@ int launch_grad(const GradCall& g) {
     r.pdd = reinterpret_cast<float*>(ws + offs[3]);
     r.du = g.du; r.ddelta = g.ddelta; r.dz = g.dz;
     r.bc_part = reinterpret_cast<float*>(ws + offs[4]);
-    r.dA = g.dA; r.dD = g.dD; r.dbias = g.dbias;
+    r.pstat = reinterpret_cast<float*>(ws + offs[5]);
     r.dim = g.dim; r.L = g.L; r.dstate = static_cast<int>(g.dstate); r.nblk = nblk;
     if (ch == 24)
         launch_rowgrad<T, 24>(g.z != nullptr, g.softplus != 0, grid, st, r);
     else
         launch_rowgrad<T, 8>(g.z != nullptr, g.softplus != 0, grid, st, r);
-    // 4. dB and dC
-    hipLaunchKernelGGL(grad_bc_reduce_kernel, dim3(static_cast<unsigned>(nblk), static_cast<unsigned>(g.batch)),
-                       blk, 0, st, r.bc_part, g.dB, g.dC, g.L, static_cast<int>(g.dstate), nblk,
-                       static_cast<int>(groups));
+    // 3. dB and dC; dA, dD and dt_bias
+    const int64_t pblocks = (2 * g.dim * (g.dstate + 2) + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(grad_bc_reduce_kernel,
+                       dim3(static_cast<unsigned>(nblk + pblocks), static_cast<unsigned>(g.batch)), blk, 0, st,
+                       r.bc_part, g.dB, g.dC, g.L, static_cast<int>(g.dstate), nblk, static_cast<int>(groups),
+                       r.pstat, g.dA, g.dD, g.dbias, g.dim, static_cast<int>(g.batch));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
     return VS_OK;

@@ -82,7 +82,7 @@ int prepare(Call& c);
 size_t scan_ws_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);
 
 int grad_channels(int64_t batch, int64_t dim);
-size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[5]);
+size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[6]);
 int validate_grad(const GradCall& g);
 
 int validate_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
