@@ -1147,10 +1147,12 @@ void rowgrad_kernel(const GradArgs a) {
     constexpr int kWaves = CH / 2;
     static_assert(CH % 4 == 0, "whole waves, and at least the 256 staging threads");
     __shared__ __attribute__((aligned(16))) float tile[2][2][2][kRowLanes][kTilePad];
-    // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap;
-    // two buffers, so that a block's sums are reduced while the waves go on
-    // to the next block (one barrier per block)
-    __shared__ __attribute__((aligned(16))) float red[2][kWaves][kWaveLanes][kTilePad];
+    // per wave and lane: the 16 steps' dB|dC sums after the 32-lane swap, as
+    // four float4 (steps 4q..4q+3) stored lane after lane, so that the
+    // writes and the summing reads are both contiguous across lanes; two
+    // buffers, so that a block's sums are reduced while the waves go on to
+    // the next block (one barrier per block)
+    __shared__ float4 red[2][kWaves][4][kWaveLanes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWaveLanes - 1);
@@ -1234,11 +1236,11 @@ void rowgrad_kernel(const GradArgs a) {
     // side = (l / 16) & 1 (the rows' direction) and state l % 16, which is
     // the chunk's [which][side][n] order
     float* const bc_chunks = a.bc_part + static_cast<size_t>(b * gridDim.x + cg) * nblk * kBcChunk;
-    // the first 256 threads store the chunk (a float4 each); the others get
-    // an out-of-range offset
-    const int chunk_off = stager ? tid * 16 : kBcChunk * 4;
-    float4* const red_lane0 = reinterpret_cast<float4*>(&red[0][tid >> 6][lane][0]);
-    float4* const red_lane1 = reinterpret_cast<float4*>(&red[1][tid >> 6][lane][0]);
+    // the first 256 threads sum and store the chunk: thread (q = tid / 64,
+    // l = tid % 64) the float4 of steps 4q..4q+3 of wave lane l, at chunk
+    // floats 16 l + 4 q; the others get an out-of-range offset
+    const int red_q = (tid >> 6) & 3;
+    const int chunk_off = stager ? (lane * 16 + red_q * 4) * 4 : kBcChunk * 4;
 
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
@@ -1423,20 +1425,18 @@ void rowgrad_kernel(const GradArgs a) {
         // writes the other sum buffer, whose reduction finished before this
         // barrier, so one barrier per block covers both.
         stage_store(buf ^ 1, sr);
-        float4* const red_lane = (blk & 1) ? red_lane1 : red_lane0;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            red_lane[q] = make_float4(sbc[4 * q], sbc[4 * q + 1], sbc[4 * q + 2], sbc[4 * q + 3]);
+            red[blk & 1][tid >> 6][q][lane] = make_float4(sbc[4 * q], sbc[4 * q + 1], sbc[4 * q + 2], sbc[4 * q + 3]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         if (stager) {
             const int rb = blk & 1;
-            const int rl = (tid >> 2) & (kWaveLanes - 1), i0 = (tid & 3) * 4;
-            float4 acc = *reinterpret_cast<const float4*>(&red[rb][0][rl][i0]);
+            float4 acc = red[rb][0][red_q][lane];
 #pragma unroll
             for (int w = 1; w < kWaves; ++w) {
-                const float4 v = *reinterpret_cast<const float4*>(&red[rb][w][rl][i0]);
+                const float4 v = red[rb][w][red_q][lane];
                 acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
             }
             const auto rc = __builtin_amdgcn_make_buffer_rsrc(bc_chunks + static_cast<size_t>(blk) * kBcChunk,
