@@ -1106,13 +1106,13 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //     contributions for the block's 16 steps. A 32-lane swap sums the wave's
 //     two rows of the same direction (dB lands in the low half of the wave,
 //     dC in the high half), LDS sums the four waves, and the workgroup
-//     stores its 1024 block sums (dB|dC x side x state x step) as one
+//     stores its 1024 block sums (dB|dC x side x step x state) as one
 //     contiguous 4 KB chunk. grad_bc_reduce_kernel then sums the chunks over
 //     the workgroups in a fixed order, so no atomics are involved and dB and
 //     dC repeat bit for bit. dA, dD and dt_bias are summed per row, stored
 //     per batch row, and summed over the batch rows by the same kernel, in
 //     order, so they repeat bit for bit as well.
-using vs::kBcChunk;               // floats per workgroup and block: [dB|dC][side][n][step]
+using vs::kBcChunk;               // floats per workgroup and block: [dB|dC][side][step][n]
 
 struct GradArgs {
     const void *u, *delta, *z, *B, *C, *dy;
@@ -1233,14 +1233,14 @@ void rowgrad_kernel(const GradArgs a) {
         }
     }
     // after the swap, lane l of a wave holds which = l / 32 (dB, dC),
-    // side = (l / 16) & 1 (the rows' direction) and state l % 16, which is
-    // the chunk's [which][side][n] order
+    // side = (l / 16) & 1 (the rows' direction) and state l % 16; the chunk
+    // is [which][side][step][state]
     float* const bc_chunks = a.bc_part + static_cast<size_t>(b * gridDim.x + cg) * nblk * kBcChunk;
     // the first 256 threads sum and store the chunk: thread (q = tid / 64,
-    // l = tid % 64) the float4 of steps 4q..4q+3 of wave lane l, at chunk
-    // floats 16 l + 4 q; the others get an out-of-range offset
+    // l = tid % 64) steps 4q..4q+3 of wave lane l, at chunk floats
+    // 256 (l / 16) + 16 step + l % 16; the others get an out-of-range offset
     const int red_q = (tid >> 6) & 3;
-    const int chunk_off = stager ? (lane * 16 + red_q * 4) * 4 : kBcChunk * 4;
+    const int chunk_off = stager ? ((lane >> 4) * 256 + red_q * 64 + (lane & 15)) * 4 : kBcChunk * 4;
 
     auto tok_pos = [&](int blk) {
         const int t = blk * kBlockTok + n;
@@ -1441,8 +1441,10 @@ void rowgrad_kernel(const GradArgs a) {
             }
             const auto rc = __builtin_amdgcn_make_buffer_rsrc(bc_chunks + static_cast<size_t>(blk) * kBcChunk,
                                                               0, kBcChunk * 4, 0x00020000);
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, acc), rc, chunk_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.x), rc, chunk_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.y), rc, chunk_off + 64, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.z), rc, chunk_off + 128, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc.w), rc, chunk_off + 192, 0, 0);
         }
     };
 
@@ -1506,15 +1508,19 @@ __global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
         else dbias[k - na - 2 * dim] = sum;
         return;
     }
-    const int n = threadIdx.x >> 4, i = threadIdx.x & 15;
+    // consecutive threads take consecutive states, so that each step's 16
+    // states are one contiguous 64-byte read
+    const int n = threadIdx.x & 15, i = threadIdx.x >> 4;
     const int64_t b = blockIdx.y;
     const int64_t tok = static_cast<int64_t>(blockIdx.x) * kBlockTok + i;
     if (n >= dstate || tok >= L) return;
     const int64_t t1 = L - 1 - tok;
-    // [which][side][n][step]: side 0 for the forward direction, 1 for the backward one
-    const size_t o0 = static_cast<size_t>(blockIdx.x) * kBcChunk + static_cast<size_t>(n) * kBlockTok + i;
+    // [which][side][step][n]: side 0 for the forward direction, 1 for the
+    // backward one; every (side, step) row of a chunk is read by the one
+    // workgroup whose tokens it holds
+    const size_t o0 = static_cast<size_t>(blockIdx.x) * kBcChunk + static_cast<size_t>(i) * kRowLanes + n;
     const size_t o1 = static_cast<size_t>(t1 / kBlockTok) * kBcChunk +
-                      static_cast<size_t>(kRowLanes + n) * kBlockTok + static_cast<size_t>(t1 % kBlockTok);
+                      static_cast<size_t>(kBlockTok + t1 % kBlockTok) * kRowLanes + n;
     constexpr size_t kC = kBcChunk / 2;
     const size_t gstride = static_cast<size_t>(nblk) * kBcChunk;
     const float* c = part + static_cast<size_t>(b) * ngroups * gstride;
