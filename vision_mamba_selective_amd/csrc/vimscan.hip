@@ -843,9 +843,15 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     });
     wg_barrier();
 
-    float* ck_row = nullptr;
-    if (CKPT)
-        ck_row = a.ckpt + ((static_cast<size_t>(b * a.dim + d) * 2 + dir) * nblk) * kRowLanes;
+    // checkpoints [batch][dim][direction][block][state]: the wave's four rows
+    // are adjacent, so one descriptor covers them; an inactive channel's
+    // lanes land past it and store nothing
+    // (built in every form; only CKPT stores through it)
+    const size_t ck_row_fl = static_cast<size_t>(nblk) * kRowLanes;
+    const __amdgpu_buffer_rsrc_t rs_ck = __builtin_amdgcn_make_buffer_rsrc(
+        a.ckpt + static_cast<size_t>(b * a.dim + (wave_nch > 0 ? wave_d0 : 0)) * 2 * ck_row_fl, 0,
+        static_cast<int>(wave_nch * 2 * ck_row_fl * 4), 0x00020000);
+    const int ck_off0 = static_cast<int>((static_cast<size_t>((d0 - wave_d0) * 2 + dir) * ck_row_fl + n) * 4);
     // One block step. `cur` holds this block's token data (loaded kTokAhead
     // steps earlier), `nxt` receives block blk + kTokAhead's; the loop below
     // rotates the sets so that no register of an in-flight load is ever
@@ -857,7 +863,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int half = blk % kBpt;
         const int p = cur.p;
         const bool ok = active && blk * kBlockTok + n < L;
-        if (CKPT && active) ck_row[blk * kRowLanes + n] = h;
+        if constexpr (CKPT)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), rs_ck, ck_off0 + blk * (kRowLanes * 4), 0, 0);
         // the other direction's partial sum, for blocks after step F (it was
         // stored at step F or earlier, before F's fence); earlier blocks load
         // entry 0 of the row instead (unused) rather than branch. Issued
