@@ -74,7 +74,8 @@ enum {
 };
 
 /* operation kinds for vs_workspace_bytes */
-enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 };
+enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3,
+       VS_OP_VIM_SAVED = 4, VS_OP_VIM_GRAD_SAVED = 5 };
 
 /* The delta_softplus argument of the scan entry points is a flags word.
  * VS_FLAG_SOFTPLUS: delta = softplus(delta_raw + dt_bias), else delta_raw +
@@ -90,7 +91,10 @@ enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3 }
 
 /* Bytes of device workspace an operation needs (VS_OP_VIM_GRAD: the
  * gradient's forward output, per-block states, partial sums and the
- * per-workgroup dB/dC block sums, about 52 bytes per element). Otherwise, in units of E =
+ * per-workgroup dB/dC block sums, about 52 bytes per element;
+ * VS_OP_VIM_SAVED: the saved-state buffer of vim_scan_bidir_fwd_saved, the
+ * first two of those, about 12 bytes per element; VS_OP_VIM_GRAD_SAVED: the
+ * workspace of vim_scan_bidir_grad_saved, the rest). Otherwise, in units of E =
  * batch*dim*seqlen elements. Direction merge: fp32 buffers of E floats,
  * one for VS_OP_VIM_BIDIR and two for VS_OP_CROSS4 (one per pair of opposite
  * directions); an fp32 y serves as the first, so fp32 needs one fewer.
@@ -255,6 +259,43 @@ int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
                         int delta_softplus, const void* dy, void* du, void* ddelta, void* dz,
                         float* dB, float* dC, float* dA, float* dD, float* ddt_bias,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * A training step's two halves with the backward's forward pass done once:
+ * vim_scan_bidir_fwd_saved computes y exactly as vim_scan_bidir does (the
+ * guide's section "2. The Bidirectional Mamba Block") and also writes what
+ * the gradient needs from the forward pass into `saved`: the merged ungated
+ * output y_f + y_b (fp32) and every recurrence's state at the start of each
+ * 16-token block. vim_scan_bidir_grad_saved is vim_scan_bidir_grad reading
+ * those instead of recomputing them; for the same inputs its outputs are
+ * the same bit for bit.
+ * vim_scan_bidir_fwd_saved:
+ *   arguments      as for vim_scan_bidir; delta_softplus takes
+ *                  VS_FLAG_SOFTPLUS only (the gradient's delta B form)
+ *   saved          at least vs_workspace_bytes(VS_OP_VIM_SAVED, ...) bytes,
+ *                  4-byte aligned; written completely, in a layout private to
+ *                  the library; it must not overlap an input or y
+ * vim_scan_bidir_grad_saved:
+ *   arguments      as for vim_scan_bidir_grad
+ *   saved          the buffer of a vim_scan_bidir_fwd_saved call on the same
+ *                  u, delta, B, C, A, Dskip, dt_bias and flag, and the same
+ *                  sizes (read only; not checked: other contents give
+ *                  meaningless gradients); it must not overlap an output or
+ *                  the workspace
+ *   workspace      at least vs_workspace_bytes(VS_OP_VIM_GRAD_SAVED, ...) bytes
+ * Both refuse sequences longer than 2^26 tokens (VS_ERR_UNSUPPORTED) and
+ * return VS_ERR_WORKSPACE for a missing or short buffer.
+ */
+int vim_scan_bidir_fwd_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                             const void* u, const void* delta, const void* z, const void* B,
+                             const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                             int delta_softplus, void* y, void* saved, size_t saved_bytes, void* stream);
+int vim_scan_bidir_grad_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                              const void* u, const void* delta, const void* z, const void* B,
+                              const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                              int delta_softplus, const void* saved, size_t saved_bytes, const void* dy,
+                              void* du, void* ddelta, void* dz, float* dB, float* dC, float* dA, float* dD,
+                              float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The linear maps around the scan, on the matrix cores (bf16 operands, fp32

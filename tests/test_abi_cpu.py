@@ -309,3 +309,50 @@ def test_chunked_refuses_what_it_does_not_chunk(nat):
     assert b"chunks" in nat.lib.vs_last_error()
     rc = f(*args, 1, 2, far(8), None, 0, None)                   # bf16 needs the workspace
     assert rc == -8
+
+
+def test_saved_pair_sizes_and_refusals(nat):
+    """The saved-state buffer and the saved gradient's workspace split the
+    gradient's workspace exactly; bad arguments are refused before any HIP
+    call: a short or missing saved buffer, the exact hold, a saved buffer
+    that overlaps an output, over-long sequences."""
+    ws = nat.lib.vs_workspace_bytes
+    for dims in ((2, 8, 33), (8, 768, 4097), (1, 1, 1)):
+        full = ws(nat.VS_OP_VIM_GRAD, *dims, nat.VS_BF16)
+        sv = ws(nat.VS_OP_VIM_SAVED, *dims, nat.VS_BF16)
+        rest = ws(nat.VS_OP_VIM_GRAD_SAVED, *dims, nat.VS_BF16)
+        assert sv > 0 and rest > 0 and sv + rest == full
+        e = dims[0] * dims[1] * dims[2]
+        assert sv >= 4 * e                          # at least the fp32 ungated output
+    assert ws(6, 2, 8, 33, nat.VS_BF16) == 0          # unknown operation
+    sv = ws(nat.VS_OP_VIM_SAVED, 2, 8, 33, nat.VS_BF16)
+    rest = ws(nat.VS_OP_VIM_GRAD_SAVED, 2, 8, 33, nat.VS_BF16)
+
+    fwd = nat.lib.vim_scan_bidir_fwd_saved
+    fargs = [2, 8, 16, 33, nat.VS_BF16, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5), None, None]
+    assert fwd(*fargs, 1, fake(6), fake(7), sv - 1, None) == -8
+    assert b"VS_OP_VIM_SAVED" in nat.lib.vs_last_error()
+    assert fwd(*fargs, 1, fake(6), None, sv, None) == -8
+    assert fwd(*fargs, 3, fake(6), fake(7), sv, None) == -6         # VS_FLAG_ZOH
+    assert fwd(*fargs, 1, fake(6), fake(0) + 64, sv, None) == -5    # saved inside u
+
+    g = nat.lib.vim_scan_bidir_grad_saved
+
+    def call(**kw):
+        a = dict(sv=fake(16), svb=sv, dy=fake(6), du=fake(7), dd=fake(8), dz=fake(9), dB=fake(10),
+                 dC=fake(11), dA=fake(12), dD=fake(13), db=fake(14), ws=fake(15), wsb=rest, sp=1)
+        a.update(kw)
+        return g(2, 8, 16, 33, nat.VS_BF16, fake(0), fake(1), fake(2), fake(3), fake(4), fake(5),
+                 None, None, a["sp"], a["sv"], a["svb"], a["dy"], a["du"], a["dd"], a["dz"], a["dB"],
+                 a["dC"], a["dA"], a["dD"], a["db"], a["ws"], a["wsb"], None)
+    assert call(sv=None) == -1
+    assert call(svb=sv - 1) == -8
+    assert call(wsb=rest - 1) == -8
+    assert call(sp=3) == -6
+    assert call(du=fake(16) + 64) == -5              # an output inside the saved buffer
+    assert call(ws=fake(16)) == -5                   # the workspace on the saved buffer
+    # both cap the sequence at 2^26 tokens (one batch row, one channel)
+    L = (1 << 26) + 1
+    big = ws(nat.VS_OP_VIM_SAVED, 1, 1, L, nat.VS_F32)
+    assert fwd(1, 1, 16, L, nat.VS_F32, far(0), far(1), None, far(2), far(3), far(4), None, None,
+               1, far(5), far(6), big, None) == -6

@@ -7,10 +7,9 @@ Tolerances (|g - g_ref| <= tol * (1 + |g_ref|)):
     forward's bound; the adjoint recurrence runs in fp32 like the forward
     one) and 2e-2 for bf16 (the final bf16 rounding dominates, as for y);
   * dB, dC, dA, dD, ddt_bias are fp32 sums over channels, batch rows and
-    steps (dB and dC in a fixed order, the others by atomic additions in any
-    order): 2e-4 for either input dtype, since the inputs are exact in fp32
-    and only the fp32 accumulation differs (the per-element sums have at
-    most a few thousand terms)."""
+    steps, taken in a fixed order: 2e-4 for either input dtype, since the
+    inputs are exact in fp32 and only the fp32 accumulation differs (the
+    per-element sums have at most a few thousand terms)."""
 import numpy as np
 import pytest
 import torch

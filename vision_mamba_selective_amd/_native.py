@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libvimscan.so")
 
 VS_F32, VS_BF16 = 0, 1
 VS_OP_VIM_BIDIR, VS_OP_CROSS4, VS_OP_1D, VS_OP_VIM_GRAD = 0, 1, 2, 3
+VS_OP_VIM_SAVED, VS_OP_VIM_GRAD_SAVED = 4, 5
 VS_NOALLOC_MAX_ELEMS = 1 << 25
 
 # names and argument types of every entry point declared in include/vimscan.h
@@ -36,6 +37,10 @@ SIGNATURES = {
                                  _P, _P, _I, _P, _P, _SZ, _P]),
     "vim_scan_bidir_grad": (_I, [_I64, _I64, _I64, _I64, _I] + [_P] * 8 + [_I] + [_P] * 9 +
                             [_P, _SZ, _P]),
+    "vim_scan_bidir_fwd_saved": (_I, [_I64, _I64, _I64, _I64, _I] + [_P] * 8 + [_I] +
+                                 [_P, _P, _SZ, _P]),
+    "vim_scan_bidir_grad_saved": (_I, [_I64, _I64, _I64, _I64, _I] + [_P] * 8 + [_I] +
+                                  [_P, _SZ] + [_P] * 9 + [_P, _SZ, _P]),
     "vmamba_cross_scan4": (_I, [_I64, _I64, _I64, _I64, _I64, _I, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _I, _P, _P, _SZ, _P]),
     "s6_scan_1d": (_I, [_I64, _I64, _I64, _I64, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I,

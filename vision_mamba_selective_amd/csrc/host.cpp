@@ -52,6 +52,15 @@ size_t scan_ws_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dty
         size_t offs[6];
         return grad_ws_bytes(batch, dim, seqlen, offs);
     }
+    if (op == VS_OP_VIM_SAVED) {
+        size_t offs[2];
+        return grad_saved_bytes(batch, dim, seqlen, offs);
+    }
+    if (op == VS_OP_VIM_GRAD_SAVED) {
+        size_t offs[4];
+        return grad_rest_bytes(batch, dim, seqlen, offs);
+    }
+    if (op != VS_OP_VIM_BIDIR && op != VS_OP_CROSS4 && op != VS_OP_1D) return 0;
     // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
     // cross-scan two; an fp32 y serves as the first. The cross-scan also
     // keeps column-major copies of u and delta (input dtype).
@@ -78,6 +87,10 @@ int validate(const Call& c) {
     if (c.chunks < 0) return fail(VS_ERR_SHAPE, "the chunk count must be >= 0");
     if (c.chunks > 1 && (c.mode != kModeVim || c.conv || c.zoh || c.per_dir))
         return fail(VS_ERR_UNSUPPORTED, "chunks: the plain Vim scan only (no ZOH)");
+    if (c.saved_fwd && c.zoh)
+        return fail(VS_ERR_UNSUPPORTED, "the saving forward takes VS_FLAG_SOFTPLUS only (delta B form)");
+    if (c.saved_fwd && c.L > kGradMaxL)
+        return fail(VS_ERR_UNSUPPORTED, "the saving forward supports sequences of up to 2^26 tokens");
     // kernels address every tensor with 32-bit byte offsets (fp32 partial
     // sums included), so each tensor must stay below 4 GiB. Every factor is
     // bounded above by now, and the products are formed only once they are
@@ -113,7 +126,8 @@ int validate(const Call& c) {
         if (overlaps(c.y, act, ins[i], in_bytes[i]))
             return fail(VS_ERR_ALIAS, "y overlaps an input");
     const size_t need = scan_ws_bytes(
-        c.mode == kModeVim ? VS_OP_VIM_BIDIR : (c.mode == kModeCross4 ? VS_OP_CROSS4 : VS_OP_1D),
+        c.saved_fwd ? VS_OP_VIM_SAVED
+                    : (c.mode == kModeVim ? VS_OP_VIM_BIDIR : (c.mode == kModeCross4 ? VS_OP_CROSS4 : VS_OP_1D)),
         c.batch, c.dim, c.L, c.dtype);
     if (need > 0 && c.ws_internal) {
         // the library's own buffer: no overlap with the caller's memory is
@@ -123,7 +137,9 @@ int validate(const Call& c) {
                                             "(VS_NOALLOC_MAX_ELEMS for bf16)");
     } else if (need > 0) {
         if (!c.ws || c.ws_bytes < need)
-            return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
+            return fail(VS_ERR_WORKSPACE, c.saved_fwd ? "saved-state buffer missing or smaller than "
+                                                        "vs_workspace_bytes(VS_OP_VIM_SAVED)"
+                                                      : "workspace missing or smaller than vs_workspace_bytes()");
         if (overlaps(c.y, act, c.ws, need)) return fail(VS_ERR_ALIAS, "y overlaps the workspace");
         for (int i = 0; i < kIns; ++i)
             if (overlaps(c.ws, need, ins[i], in_bytes[i]))
@@ -154,27 +170,49 @@ int grad_channels(int64_t batch, int64_t dim) {
     return batch * ((dim + 23) / 24) >= kNumCUs ? 24 : 8;
 }
 
-// workspace of the gradient: [s: fp32 E][checkpoints: fp32 rows*nblk*16]
-// [du partials: fp32 E][ddelta partials: fp32 E][dB/dC chunks], each 256-byte
-// aligned. Sizes must have passed the 2^30-element checks.
-size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[6]) {
+// The gradient's buffers, each region 256-byte aligned. Sizes must have
+// passed the 2^30-element checks.
+namespace {
+size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+}
+
+// saved part: [s: fp32 E, the merged ungated forward output][checkpoints:
+// fp32 [batch][dim][2][nblk][16], the state at every block start]
+size_t grad_saved_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[2]) {
     const size_t elems = static_cast<size_t>(batch * dim * L);
     const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
     const size_t ck = static_cast<size_t>(batch * dim) * 2 * nblk * kRowLanes;
+    offs[0] = 0;
+    offs[1] = al256(4 * elems);
+    return offs[1] + al256(4 * ck);
+}
+
+// rest: [du partials: fp32 E][ddelta partials: fp32 E][dB/dC chunks]
+// [per batch row: dA [2][dim][dstate], dD [2][dim], ddt_bias [2][dim], sized
+// for the largest dstate]
+size_t grad_rest_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[4]) {
+    const size_t elems = static_cast<size_t>(batch * dim * L);
+    const size_t nblk = static_cast<size_t>((L + kBlockTok - 1) / kBlockTok);
     const int ch = grad_channels(batch, dim);
     const size_t groups = static_cast<size_t>((dim + ch - 1) / ch);
     const size_t chunks = static_cast<size_t>(batch) * groups * nblk * kBcChunk;
-    auto al = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     size_t off = 0;
-    offs[0] = off; off += al(4 * elems);     // merged ungated forward output
-    offs[1] = off; off += al(4 * ck);        // block-start states
-    offs[2] = off; off += al(4 * elems);     // du partials
-    offs[3] = off; off += al(4 * elems);     // ddelta partials
-    offs[4] = off; off += al(4 * chunks);    // dB/dC chunks
-    // per batch row: dA [2][dim][dstate], dD [2][dim], ddt_bias [2][dim]
-    // (sized for the largest dstate)
-    offs[5] = off; off += al(4 * static_cast<size_t>(batch * 2 * dim * (VS_MAX_DSTATE + 2)));
+    offs[0] = off; off += al256(4 * elems);
+    offs[1] = off; off += al256(4 * elems);
+    offs[2] = off; off += al256(4 * chunks);
+    offs[3] = off; off += al256(4 * static_cast<size_t>(batch * 2 * dim * (VS_MAX_DSTATE + 2)));
     return off;
+}
+
+// the whole gradient workspace: the saved part, then the rest
+size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[6]) {
+    size_t so[2], ro[4];
+    const size_t saved = grad_saved_bytes(batch, dim, L, so);
+    const size_t rest = grad_rest_bytes(batch, dim, L, ro);
+    offs[0] = so[0];
+    offs[1] = so[1];
+    for (int i = 0; i < 4; ++i) offs[2 + i] = saved + ro[i];
+    return saved + rest;
 }
 
 int validate_grad(const GradCall& g) {
@@ -201,25 +239,29 @@ int validate_grad(const GradCall& g) {
     const void* acts[] = {g.u, g.delta, g.z, g.B, g.C, g.dy, g.du, g.ddelta, g.dz};
     for (const void* p : acts)
         if (p && !aligned(p, es)) return fail(VS_ERR_ALIGN, "activation pointer misaligned");
-    const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
+    const void* fps[] = {g.A, g.Dskip, g.dt_bias, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws, g.saved};
     for (const void* p : fps)
         if (p && !aligned(p, 4)) return fail(VS_ERR_ALIGN, "fp32 pointer misaligned");
     size_t offs[6];
-    const size_t need = grad_ws_bytes(g.batch, g.dim, g.L, offs);
+    const size_t need = g.saved ? grad_rest_bytes(g.batch, g.dim, g.L, offs)
+                                : grad_ws_bytes(g.batch, g.dim, g.L, offs);
     if (!g.ws || g.ws_bytes < need)
         return fail(VS_ERR_WORKSPACE, "workspace missing or smaller than vs_workspace_bytes()");
+    const size_t saved_need = grad_saved_bytes(g.batch, g.dim, g.L, offs);
+    if (g.saved && g.saved_bytes < saved_need)
+        return fail(VS_ERR_WORKSPACE, "saved-state buffer smaller than vs_workspace_bytes(VS_OP_VIM_SAVED)");
     // no output (nor the workspace) may overlap an input or another output
     const size_t act = static_cast<size_t>(elems) * es;
     const size_t bc_in = static_cast<size_t>(g.batch * g.dstate * g.L) * es;
     const size_t bcf = static_cast<size_t>(g.batch * g.dstate * g.L) * 4;
     const size_t pa = static_cast<size_t>(2 * g.dim * g.dstate) * 4;
     const size_t pd = static_cast<size_t>(2 * g.dim) * 4;
-    const void* ins[] = {g.u, g.delta, g.z, g.B, g.C, g.A, g.Dskip, g.dt_bias, g.dy};
-    const size_t in_b[] = {act, act, act, bc_in, bc_in, pa, pd, pd, act};
+    const void* ins[] = {g.u, g.delta, g.z, g.B, g.C, g.A, g.Dskip, g.dt_bias, g.dy, g.saved};
+    const size_t in_b[] = {act, act, act, bc_in, bc_in, pa, pd, pd, act, g.saved ? saved_need : 0};
     const void* outs[] = {g.du, g.ddelta, g.dz, g.dB, g.dC, g.dA, g.dD, g.dbias, g.ws};
     const size_t out_b[] = {act, act, act, bcf, bcf, pa, pd, pd, need};
     for (int i = 0; i < 9; ++i) {
-        for (int j = 0; j < 9; ++j)
+        for (int j = 0; j < 10; ++j)
             if (overlaps(outs[i], out_b[i], ins[j], in_b[j]))
                 return fail(VS_ERR_ALIAS, "a gradient output or the workspace overlaps an input");
         for (int j = i + 1; j < 9; ++j)

@@ -294,9 +294,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CHUNK || (MODE == kModeVim && !CONV && !CKPT && !ZOH),
                   "chunks: the plain Vim scan only");
     // CKPT (the gradient's forward pass): store every row's state at each
-    // block start and, in place of y, the merged ungated sum in the partial
-    // buffer (fp32)
-    static_assert(!CKPT || (MODE == kModeVim && !GATE), "checkpoints: ungated Vim only");
+    // block start and the merged ungated sum in the partial buffer (fp32);
+    // y (gated) is written as well when it is given
+    static_assert(!CKPT || MODE == kModeVim, "checkpoints: Vim only");
     // ZOH: the exact zero-order hold B_bar = (exp(delta A) - 1) / A B ("Discretization
     // via Zero-Order Hold (ZOH)") in place of delta B
     static_assert(!(ZOH && CKPT), "the gradient uses delta B");
@@ -429,7 +429,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const __amdgpu_buffer_rsrc_t rs_u = wave_rsrc(a.u, kEs, a.u_dir_off);
     const __amdgpu_buffer_rsrc_t rs_dl = wave_rsrc(a.delta, kEs, a.dl_dir_off);
     const __amdgpu_buffer_rsrc_t rs_z = wave_rsrc(GATE ? a.z : a.u, kEs, 0u);
-    const __amdgpu_buffer_rsrc_t rs_y = wave_rsrc(CKPT ? a.u : a.y, kEs, 0u);
+    // a checkpointing pass without y gets a descriptor that covers nothing:
+    // its y stores are dropped
+    const bool y_none = CKPT && a.y == nullptr;
+    const __amdgpu_buffer_rsrc_t rs_y = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(static_cast<const char*>(y_none ? a.u : a.y)) + wave_base * kEs, 0,
+        y_none ? 0 : static_cast<int>(wave_el * kEs), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_p = wave_rsrc(a.partial, 4u, 0u);
     // an inactive channel's lanes land past the wave's rows (no store ever
     // uses them)
@@ -935,7 +940,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         auto finish = [&](float sum, int pp) {
             if (kRun) {
                 if (CKPT) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rs_p, poff(pp), 0, 0);
-                else rstore(rs_y, pp, sum * gate);
+                rstore(rs_y, pp, sum * gate);
             } else if (MODE == kModeCross4 || CKPT) {
                 *part_at(pp) = sum;
             } else {
@@ -969,7 +974,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
                 if (kRun) {
                     // finish through the element pointer as well
                     if (CKPT) *part_at(p) = yk + other;
-                    else st(y_at(p), 0, (yk + other) * gate);
+                    if (!y_none) st(y_at(p), 0, (yk + other) * gate);
                 } else {
                     finish(yk + other, p);
                 }
@@ -1705,6 +1710,8 @@ int launch_t(const Call& c) {
 // ---- gradient of the Vim scan (workspace layout: vs::grad_ws_bytes)
 using vs::grad_channels;
 using vs::grad_ws_bytes;
+using vs::grad_saved_bytes;
+using vs::grad_rest_bytes;
 
 template <typename T, int CH>
 void launch_rowgrad(bool gate, bool softplus, dim3 grid, hipStream_t st, const GradArgs& r) {
@@ -1719,13 +1726,60 @@ void launch_rowgrad(bool gate, bool softplus, dim3 grid, hipStream_t st, const G
         hipLaunchKernelGGL((rowgrad_kernel<T, false, false, CH>), grid, blk, 0, st, r);
 }
 
+// The checkpointing forward pass (rowscan_kernel with CKPT): the merged
+// ungated output s (fp32) and the state at every block start into the saved
+// buffer, and the gated y as well when y is given.
+template <typename T>
+void launch_ckpt_forward(const void* u, const void* delta, const void* z, const void* B, const void* C,
+                         const float* A, const float* Dskip, const float* dt_bias, int softplus, void* y,
+                         float* sbuf, float* ckpt, int64_t batch, int64_t dim, int64_t dstate, int64_t L,
+                         hipStream_t st) {
+    ScanArgs a{};
+    a.u = u; a.delta = delta; a.z = z; a.B = B; a.C = C;
+    a.A = A; a.Dskip = Dskip; a.dt_bias = dt_bias; a.y = y;
+    a.partial = sbuf; a.ckpt = ckpt;
+    a.dim = dim; a.L = L; a.dstate = static_cast<int>(dstate);
+    a.softplus = softplus; a.nblk = static_cast<int>((L + kBlockTok - 1) / kBlockTok);
+    constexpr int kFwdCh = 8;      // rowscan_kernel (Vim): 8 channels x 2 directions per workgroup
+    const dim3 fgrid(static_cast<unsigned>((dim + kFwdCh - 1) / kFwdCh), static_cast<unsigned>(batch));
+    const dim3 blk(kThreads);
+    if (z && softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, true, false, true>), fgrid, blk, 0, st, a);
+    else if (z)
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, true, false, false, true>), fgrid, blk, 0, st, a);
+    else if (softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), fgrid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), fgrid, blk, 0, st, a);
+}
+
+// vim_scan_bidir_fwd_saved: y and the saved buffer (c.ws)
+template <typename T>
+int launch_fwd_saved(const Call& c) {
+    size_t so[2];
+    grad_saved_bytes(c.batch, c.dim, c.L, so);
+    char* sv = static_cast<char*>(c.ws);
+    launch_ckpt_forward<T>(c.u, c.delta, c.z, c.B, c.C, c.A, c.Dskip, c.dt_bias, c.softplus, c.y,
+                           reinterpret_cast<float*>(sv + so[0]), reinterpret_cast<float*>(sv + so[1]),
+                           c.batch, c.dim, c.dstate, c.L, static_cast<hipStream_t>(c.stream));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VS_ERR_HIP, std::string("kernel launch: ") + hipGetErrorString(e));
+    return VS_OK;
+}
+
 template <typename T>
 int launch_grad(const GradCall& g) {
-    size_t offs[6];
-    grad_ws_bytes(g.batch, g.dim, g.L, offs);
+    // s and the checkpoints come from the saved buffer of a saving forward
+    // call, or from the first part of the workspace, filled here
+    size_t so[2], ro[4];
+    const size_t saved_size = grad_saved_bytes(g.batch, g.dim, g.L, so);
+    grad_rest_bytes(g.batch, g.dim, g.L, ro);
     char* ws = static_cast<char*>(g.ws);
-    float* sbuf = reinterpret_cast<float*>(ws + offs[0]);
-    float* ckpt = reinterpret_cast<float*>(ws + offs[1]);
+    // the kernels only read s and the checkpoints of a saved buffer
+    char* sv = g.saved ? const_cast<char*>(static_cast<const char*>(g.saved)) : ws;
+    char* rest = g.saved ? ws : ws + saved_size;
+    float* sbuf = reinterpret_cast<float*>(sv + so[0]);
+    float* ckpt = reinterpret_cast<float*>(sv + so[1]);
     hipStream_t st = static_cast<hipStream_t>(g.stream);
     const dim3 blk(kThreads);
     const int ch = grad_channels(g.batch, g.dim);
@@ -1733,29 +1787,20 @@ int launch_grad(const GradCall& g) {
     const dim3 grid(groups, static_cast<unsigned>(g.batch));
     const int nblk = static_cast<int>((g.L + kBlockTok - 1) / kBlockTok);
     // 1. forward pass: merged ungated output (fp32) and the states at every
-    //    block start
-    ScanArgs a{};
-    a.u = g.u; a.delta = g.delta; a.z = nullptr; a.B = g.B; a.C = g.C;
-    a.A = g.A; a.Dskip = g.Dskip; a.dt_bias = g.dt_bias; a.y = nullptr;
-    a.partial = sbuf; a.ckpt = ckpt;
-    a.dim = g.dim; a.L = g.L; a.dstate = static_cast<int>(g.dstate);
-    a.softplus = g.softplus; a.nblk = nblk;
-    constexpr int kFwdCh = 8;      // rowscan_kernel (Vim): 8 channels x 2 directions per workgroup
-    const dim3 fgrid(static_cast<unsigned>((g.dim + kFwdCh - 1) / kFwdCh), static_cast<unsigned>(g.batch));
-    if (g.softplus)
-        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, true, false, true>), fgrid, blk, 0, st, a);
-    else
-        hipLaunchKernelGGL((rowscan_kernel<T, kModeVim, false, false, false, true>), fgrid, blk, 0, st, a);
+    //    block start (not needed after a saving forward call)
+    if (!g.saved)
+        launch_ckpt_forward<T>(g.u, g.delta, nullptr, g.B, g.C, g.A, g.Dskip, g.dt_bias, g.softplus, nullptr,
+                               sbuf, ckpt, g.batch, g.dim, g.dstate, g.L, st);
     // 2. reverse pass
     GradArgs r{};
     r.u = g.u; r.delta = g.delta; r.z = g.z; r.B = g.B; r.C = g.C; r.dy = g.dy;
     r.A = g.A; r.Dskip = g.Dskip; r.dt_bias = g.dt_bias;
     r.s = sbuf; r.ckpt = ckpt;
-    r.pdu = reinterpret_cast<float*>(ws + offs[2]);
-    r.pdd = reinterpret_cast<float*>(ws + offs[3]);
+    r.pdu = reinterpret_cast<float*>(rest + ro[0]);
+    r.pdd = reinterpret_cast<float*>(rest + ro[1]);
     r.du = g.du; r.ddelta = g.ddelta; r.dz = g.dz;
-    r.bc_part = reinterpret_cast<float*>(ws + offs[4]);
-    r.pstat = reinterpret_cast<float*>(ws + offs[5]);
+    r.bc_part = reinterpret_cast<float*>(rest + ro[2]);
+    r.pstat = reinterpret_cast<float*>(rest + ro[3]);
     r.dim = g.dim; r.L = g.L; r.dstate = static_cast<int>(g.dstate); r.nblk = nblk;
     if (ch == 24)
         launch_rowgrad<T, 24>(g.z != nullptr, g.softplus != 0, grid, st, r);
@@ -1891,6 +1936,36 @@ int vim_scan_bidir_grad(int64_t batch, int64_t dim, int64_t dstate, int64_t seql
     GradCall g{batch, dim, dstate, seqlen, dtype, u, delta, z, B, C, A, Dskip, dt_bias,
                delta_softplus, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
                workspace, workspace_bytes, stream};
+    const int rc = vs::validate_grad(g);
+    if (rc != VS_OK) return rc;
+    return dtype == VS_BF16 ? launch_grad<uint16_t>(g) : launch_grad<float>(g);
+}
+
+int vim_scan_bidir_fwd_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                             const void* u, const void* delta, const void* z, const void* B,
+                             const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                             int delta_softplus, void* y, void* saved, size_t saved_bytes, void* stream) {
+    Call c{kModeVim, batch, dim, dstate, seqlen, 0, 0, dtype, 0, u, delta, z, B, C,
+           A, Dskip, dt_bias, delta_softplus, y, saved, saved_bytes, stream};
+    c.saved_fwd = true;
+    const int rc = vs::prepare(c);
+    if (rc != VS_OK) return rc;
+    return dtype == VS_BF16 ? launch_fwd_saved<uint16_t>(c) : launch_fwd_saved<float>(c);
+}
+
+int vim_scan_bidir_grad_saved(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int dtype,
+                              const void* u, const void* delta, const void* z, const void* B,
+                              const void* C, const float* A, const float* Dskip, const float* dt_bias,
+                              int delta_softplus, const void* saved, size_t saved_bytes, const void* dy,
+                              void* du, void* ddelta, void* dz, float* dB, float* dC, float* dA, float* dD,
+                              float* ddt_bias, void* workspace, size_t workspace_bytes, void* stream) {
+    vs::clear_error();
+    if (!saved) return fail(VS_ERR_NULL, "saved must not be NULL");
+    GradCall g{batch, dim, dstate, seqlen, dtype, u, delta, z, B, C, A, Dskip, dt_bias,
+               delta_softplus, dy, du, ddelta, dz, dB, dC, dA, dD, ddt_bias,
+               workspace, workspace_bytes, stream};
+    g.saved = saved;
+    g.saved_bytes = saved_bytes;
     const int rc = vs::validate_grad(g);
     if (rc != VS_OK) return rc;
     return dtype == VS_BF16 ? launch_grad<uint16_t>(g) : launch_grad<float>(g);

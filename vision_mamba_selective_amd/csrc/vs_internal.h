@@ -44,6 +44,7 @@ struct Call {
     bool zoh = false;               // exact zero-order-hold B_bar
     int chunks = 0;                 // Vim: chunks per sequence (0: the library's choice)
     bool ws_internal = false;       // the workspace is the library's own (ws_bytes = its capacity)
+    bool saved_fwd = false;         // vim_scan_bidir_fwd_saved: ws is the saved-state buffer
 };
 
 struct GradCall {
@@ -58,6 +59,8 @@ struct GradCall {
     void* ws;
     size_t ws_bytes;
     void* stream;
+    const void* saved = nullptr;    // vim_scan_bidir_grad_saved: the forward's saved states
+    size_t saved_bytes = 0;
 };
 
 // error record of the calling thread (vs_last_error)
@@ -82,6 +85,11 @@ int prepare(Call& c);
 size_t scan_ws_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);
 
 int grad_channels(int64_t batch, int64_t dim);
+// the gradient's buffers: the saved part [s][checkpoints] (written by the
+// forward pass) and the rest [du partials][ddelta partials][dB/dC chunks]
+// [per-batch dA, dD, dt_bias]; the full workspace is the two back to back
+size_t grad_saved_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[2]);
+size_t grad_rest_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[4]);
 size_t grad_ws_bytes(int64_t batch, int64_t dim, int64_t L, size_t offs[6]);
 int validate_grad(const GradCall& g);
 

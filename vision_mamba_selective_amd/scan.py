@@ -254,6 +254,77 @@ def vim_scan_bidir_grad(u, delta, z, B, C, A, Dskip, dt_bias, dy, delta_softplus
     return out
 
 
+def vim_scan_bidir_fwd_saved(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True,
+                             out=None, saved=None):
+    """vim_scan_bidir (delta B form) that also fills the saved-state buffer a
+    later vim_scan_bidir_grad_saved call on the same inputs reads instead of
+    re-running the forward pass. Returns (y, saved); saved is an opaque
+    uint8 tensor of vs_workspace_bytes(VS_OP_VIM_SAVED) bytes."""
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    y = torch.empty_like(u) if out is None else out
+    _act("out", y, (batch, dim, L), dt, dev)
+    sv, sv_bytes = _workspace(nat.VS_OP_VIM_SAVED, batch, dim, L, dt, dev, saved)
+    rc = nat.lib.vim_scan_bidir_fwd_saved(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                          _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                          _ptr(dt_bias), int(bool(delta_softplus)), _ptr(y), _ptr(sv),
+                                          sv_bytes, _stream(dev))
+    nat.check("vim_scan_bidir_fwd_saved", rc)
+    return y, sv
+
+
+def vim_scan_bidir_grad_saved(u, delta, z, B, C, A, Dskip, dt_bias, saved, dy, delta_softplus=True,
+                              workspace=None):
+    """vim_scan_bidir_grad with the forward pass read from `saved`, the buffer
+    of a vim_scan_bidir_fwd_saved call on the same inputs. Returns the same
+    dict as vim_scan_bidir_grad."""
+    batch, dim, L = u.shape
+    dstate = A.shape[-1]
+    dt, dev = u.dtype, u.device
+    if dt not in _DTYPES:
+        raise TypeError("unsupported dtype %s" % dt)
+    for name, t in (("u", u), ("delta", delta), ("z", z), ("dy", dy)):
+        if t is not None:
+            _act(name, t, (batch, dim, L), dt, dev)
+    _act("B", B, (batch, dstate, L), dt, dev)
+    _act("C", C, (batch, dstate, L), dt, dev)
+    _param("A", A, (2, dim, dstate), dev, optional=False)
+    _param("Dskip", Dskip, (2, dim), dev)
+    _param("dt_bias", dt_bias, (2, dim), dev)
+    need = workspace_bytes(nat.VS_OP_VIM_SAVED, batch, dim, L, dt)
+    if (saved is None or saved.device != dev or not saved.is_contiguous()
+            or saved.numel() * saved.element_size() < need):
+        raise ValueError("saved must be the contiguous %d-byte buffer of vim_scan_bidir_fwd_saved" % need)
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+               dz=None if z is None else torch.empty_like(u),
+               dB=torch.empty(batch, dstate, L, **f32), dC=torch.empty(batch, dstate, L, **f32),
+               dA=torch.empty(2, dim, dstate, **f32), dD=torch.empty(2, dim, **f32),
+               ddt_bias=torch.empty(2, dim, **f32))
+    ws, ws_bytes = _workspace(nat.VS_OP_VIM_GRAD_SAVED, batch, dim, L, dt, dev, workspace)
+    rc = nat.lib.vim_scan_bidir_grad_saved(batch, dim, dstate, L, _DTYPES[dt], _ptr(u), _ptr(delta),
+                                           _ptr(z), _ptr(B), _ptr(C), _ptr(A), _ptr(Dskip),
+                                           _ptr(dt_bias), int(bool(delta_softplus)), _ptr(saved),
+                                           saved.numel() * saved.element_size(), _ptr(dy),
+                                           _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]),
+                                           _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dA"]),
+                                           _ptr(out["dD"]), _ptr(out["ddt_bias"]), _ptr(ws), ws_bytes,
+                                           _stream(dev))
+    nat.check("vim_scan_bidir_grad_saved", rc)
+    return out
+
+
 def vmamba_cross_scan4(u, delta, z, B, C, A, H, W, Dskip=None, dt_bias=None,
                        delta_softplus=True, zoh=False, out=None, workspace=None):
     """VMamba four-direction cross-scan of an H x W grid.
