@@ -83,6 +83,10 @@ def parse():
     p.add_argument("--grad", action="store_true",
                    help="time vim_scan_bidir_grad: the reverse-mode gradient of the scan for a "
                         "synthetic upstream gradient (forward recompute + adjoint pass)")
+    p.add_argument("--train", action="store_true",
+                   help="time one training step of the scan: vim_scan_bidir_fwd_saved (y and the "
+                        "states the gradient needs) then vim_scan_bidir_grad_saved (the gradient "
+                        "from them) for a synthetic upstream gradient")
     p.add_argument("--zoh", action="store_true",
                    help="exact zero-order-hold B_bar = (exp(delta A) - 1) / A B (VS_FLAG_ZOH) "
                         "instead of delta B")
@@ -135,19 +139,20 @@ def main():
 
     idx = wlm.HEADLINE if args.workload is None else args.workload
     wl = wlm.WORKLOADS[idx]
-    if (args.conv or args.grad or args.dirs) and wl.kind != "vim":
-        print("--conv, --grad and --dirs apply to the Vim workloads only", file=sys.stderr)
+    if (args.conv or args.grad or args.dirs or args.train) and wl.kind != "vim":
+        print("--conv, --grad, --train and --dirs apply to the Vim workloads only", file=sys.stderr)
         sys.exit(2)
-    if args.conv + args.grad + args.dirs > 1:
-        print("--conv, --grad and --dirs are separate measurements", file=sys.stderr)
+    if args.conv + args.grad + args.dirs + args.train > 1:
+        print("--conv, --grad, --train and --dirs are separate measurements", file=sys.stderr)
         sys.exit(2)
     if args.chunks is not None and (wl.kind != "vim" or args.conv or args.grad or args.dirs
-                                    or args.zoh):
+                                    or args.zoh or args.train):
         print("--chunks applies to the plain Vim scan", file=sys.stderr)
         sys.exit(2)
-    if args.zoh and args.grad:
+    if args.zoh and (args.grad or args.train):
         print("the gradient uses the delta B form; --zoh is a forward option", file=sys.stderr)
         sys.exit(2)
+    backward = args.grad or args.train
     tdt = torch.bfloat16 if wl.dtype == wlm.BF16 else torch.float32
     print("bench: workload %s" % wl.name, file=sys.stderr, flush=True)
 
@@ -162,7 +167,7 @@ def main():
     base = dict(u=up(inp.u, tdt), delta=up(inp.delta, tdt), z=up(inp.z, tdt), B=up(inp.B, tdt),
                 C=up(inp.C, tdt), A=up(inp.A, torch.float32), D=up(inp.D, torch.float32),
                 bias=up(inp.dt_bias, torch.float32))
-    if args.grad:
+    if backward:
         grng = np.random.default_rng(wl.seed + 600)
         gy = grng.standard_normal(inp.u.shape).astype(np.float32)
         base["dy"] = up(wlm.round_bf16(gy) if wl.dtype == wlm.BF16 else gy, tdt)
@@ -183,13 +188,16 @@ def main():
         t = {k: (None if v is None else (v if s == 0 else v.clone())) for k, v in base.items()}
         t["y"] = torch.empty(wl.batch, wl.dim, wl.seqlen, dtype=tdt, device=dev)
         t["ws"] = None
-        op = 3 if args.grad else (0 if wl.kind == "vim" else 1)
+        op = 3 if args.grad else (5 if args.train else (0 if wl.kind == "vim" else 1))
         need = vms.workspace_bytes(op, wl.batch, wl.dim, wl.seqlen, tdt)
         if need:
             t["ws"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        if args.train:
+            t["saved"] = torch.empty(vms.workspace_bytes(4, wl.batch, wl.dim, wl.seqlen, tdt),
+                                     dtype=torch.uint8, device=dev)
         sets.append(t)
 
-    if args.grad:
+    if backward:
         for t in sets:
             t["g"] = dict(du=torch.empty_like(t["u"]), ddelta=torch.empty_like(t["u"]),
                           dz=None if t["z"] is None else torch.empty_like(t["u"]),
@@ -211,9 +219,27 @@ def main():
                 p(t["ws"]), t["ws"].numel(), torch.cuda.current_stream(dev).cuda_stream)
             nat.check("vim_scan_bidir_grad", rc)
 
+        def train_call(t):
+            g = t["g"]
+            p = lambda x: None if x is None else x.data_ptr()
+            dtc = nat.VS_BF16 if wl.dtype == wlm.BF16 else nat.VS_F32
+            st = torch.cuda.current_stream(dev).cuda_stream
+            ins = (p(t["u"]), p(t["delta"]), p(t["z"]), p(t["B"]), p(t["C"]), p(t["A"]), p(t["D"]),
+                   p(t["bias"]), 1)
+            rc = nat.lib.vim_scan_bidir_fwd_saved(wl.batch, wl.dim, wl.dstate, wl.seqlen, dtc, *ins,
+                                                  p(t["y"]), p(t["saved"]), t["saved"].numel(), st)
+            nat.check("vim_scan_bidir_fwd_saved", rc)
+            rc = nat.lib.vim_scan_bidir_grad_saved(
+                wl.batch, wl.dim, wl.dstate, wl.seqlen, dtc, *ins, p(t["saved"]), t["saved"].numel(),
+                p(t["dy"]), p(g["du"]), p(g["ddelta"]), p(g["dz"]), p(g["dB"]), p(g["dC"]), p(g["dA"]),
+                p(g["dD"]), p(g["db"]), p(t["ws"]), t["ws"].numel(), st)
+            nat.check("vim_scan_bidir_grad_saved", rc)
+
     def step(t):
         if args.grad:
             grad_call(t)
+        elif args.train:
+            train_call(t)
         elif args.conv:
             vms.vim_scan_bidir_conv(t["u"], t["cw"], t["cb"], t["delta"], t["z"], t["B"], t["C"],
                                     t["A"], t["D"], t["bias"], out=t["y"], workspace=t["ws"],
@@ -283,6 +309,8 @@ def main():
     tc = wl.tokens_channels
     value = tc / (ms_per_step * 1e-3) / 1e9
     alg_bytes = wl.grad_algorithmic_bytes() if args.grad else wl.algorithmic_bytes()
+    if args.train:
+        alg_bytes = wl.algorithmic_bytes() + wl.grad_algorithmic_bytes()
     if args.dirs:   # the second copies of u, delta, B and C
         alg_bytes += 2 * tc * wl.act_bytes + 2 * wl.batch * wl.dstate * wl.seqlen * wl.act_bytes
     hbm_gbs = alg_bytes / kern_avg_s / 1e9
@@ -290,6 +318,9 @@ def main():
     upd_rate = updates / kern_avg_s
     flops_per_update = GRAD_FLOPS_PER_UPDATE if args.grad else FLOPS_PER_UPDATE
     slots_per_update = GRAD_SLOTS_PER_UPDATE if args.grad else SLOTS_PER_UPDATE
+    if args.train:      # the forward's arithmetic and the gradient's, per update
+        flops_per_update = FLOPS_PER_UPDATE + GRAD_FLOPS_PER_UPDATE
+        slots_per_update = SLOTS_PER_UPDATE + GRAD_SLOTS_PER_UPDATE
     tflops = flops_per_update * upd_rate / 1e12
     upd_peak = LANE_SLOTS / slots_per_update
 
@@ -299,6 +330,7 @@ def main():
             with open(PROFILE_TRAFFIC) as f:
                 tr = json.load(f)
             rec = tr.get(wl.name + ("+conv" if args.conv else "") + ("+grad" if args.grad else "")
+                         + ("+train" if args.train else "")
                          + ("+dirs" if args.dirs else "") + ("+zoh" if args.zoh else ""))
             if rec and rec.get("kernel_sha") == kernel_hash():
                 traffic = rec.get("bytes_per_launch")
@@ -322,7 +354,9 @@ def main():
                    "d_state": wl.dstate, "seq_len": wl.seqlen, "directions": wl.ndir,
                    "state_dtype": "f32", "input_sets_rotated": nsets,
                    "front_end": "conv1d k3 + silu, fused" if args.conv else "none",
-                   "pass": "gradient (forward recompute + adjoint)" if args.grad else "forward",
+                   "pass": ("gradient (forward recompute + adjoint)" if args.grad else
+                            ("training step (saving forward + gradient from the saved states)"
+                             if args.train else "forward")),
                    "discretization": "exact zero-order hold" if args.zoh else "delta B",
                    "inputs": "per-direction u, delta, B, C" if args.dirs else "shared",
                    "chunks": "library's choice" if args.chunks in (None, 0) else args.chunks,
@@ -367,12 +401,12 @@ def main():
         if args.conv:
             conv = (base["cw"].cpu().numpy(), base["cb"].cpu().numpy())
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv,
-                                           base["dy"].float().cpu().numpy() if args.grad else None,
-                                           zoh=args.zoh, dirs=args.dirs)
+                                           base["dy"].float().cpu().numpy() if backward else None,
+                                           zoh=args.zoh, dirs=args.dirs, train=args.train)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False):
+def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False, train=False):
     """The fp64 oracle, as it stands, on the host cores of this machine."""
     import numpy as np
     import oracle
@@ -388,6 +422,9 @@ def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False):
           flush=True)
     oracle.load()
     t0 = time.perf_counter()
+    if train:       # the forward, then the gradient
+        desc += ", forward then gradient"
+        oracle.run_inputs(sample, nthreads=threads)
     if dy is not None:
         gy = dy[:sample.wl.batch, :sample.wl.dim]
         oracle.vim_bidir_grad(sample.u, sample.delta, sample.z, sample.B, sample.C, sample.A,
