@@ -108,6 +108,18 @@ void workspace_sizes() {
     // batch row for the largest dstate
     const size_t g2 = vs::grad_ws_bytes(3, 5, 7, offs);
     CHECK(g2 - offs[5] >= size_t(4) * 3 * 2 * 5 * (VS_MAX_DSTATE + 2));
+    // the saved part and the rest add up to the whole, at every size the
+    // entry points accept, the largest included
+    const int64_t dims[][3] = {{1, 1, 1}, {8, 768, 4097}, {1, 1, int64_t(1) << 26}, {65535, 16, 1023}};
+    for (const auto& d : dims) {
+        const size_t whole = vs::scan_ws_bytes(VS_OP_VIM_GRAD, d[0], d[1], d[2], VS_BF16);
+        const size_t sv = vs::scan_ws_bytes(VS_OP_VIM_SAVED, d[0], d[1], d[2], VS_BF16);
+        const size_t rest = vs::scan_ws_bytes(VS_OP_VIM_GRAD_SAVED, d[0], d[1], d[2], VS_BF16);
+        CHECK(whole > 0 && sv > 0 && rest > 0 && sv + rest == whole);
+        CHECK(sv >= size_t(4) * d[0] * d[1] * d[2]);
+    }
+    CHECK(vs::scan_ws_bytes(VS_OP_VIM_SAVED, kMax, 2, 2, VS_BF16) == 0);
+    CHECK(vs::scan_ws_bytes(7, 8, 768, 4097, VS_BF16) == 0);
 }
 
 void grad_validation() {
@@ -126,6 +138,33 @@ void grad_validation() {
     vs::GradCall alias = g;
     alias.du = alias.dz;
     CHECK(vs::validate_grad(alias) == VS_ERR_ALIAS);
+    // reading a saved buffer: it is an input (no output may overlap it),
+    // and the workspace is then only the rest
+    vs::GradCall sv = g;
+    sv.saved = fake(18);
+    sv.saved_bytes = size_t(1) << 40;
+    sv.ws_bytes = vs::scan_ws_bytes(VS_OP_VIM_GRAD_SAVED, 8, 768, 4097, VS_BF16);
+    CHECK(vs::validate_grad(sv) == VS_OK);
+    vs::GradCall short_sv = sv;
+    short_sv.saved_bytes = vs::scan_ws_bytes(VS_OP_VIM_SAVED, 8, 768, 4097, VS_BF16) - 1;
+    CHECK(vs::validate_grad(short_sv) == VS_ERR_WORKSPACE);
+    vs::GradCall on_sv = sv;
+    on_sv.dB = static_cast<float*>(fake(18));
+    CHECK(vs::validate_grad(on_sv) == VS_ERR_ALIAS);
+    // the saving forward: the saved buffer stands for the workspace
+    vs::Call c{vs::kModeVim, 8, 768, 16, 4097, 0, 0, VS_BF16, 0, fake(0), fake(1), fake(2), fake(3),
+               fake(4), static_cast<const float*>(fake(5)), nullptr, nullptr, VS_FLAG_SOFTPLUS,
+               fake(9), fake(18), size_t(1) << 40, nullptr};
+    c.saved_fwd = true;
+    CHECK(vs::prepare(c) == VS_OK);
+    vs::Call zoh = c;
+    zoh.softplus = VS_FLAG_SOFTPLUS | VS_FLAG_ZOH;
+    zoh.saved_fwd = true;
+    CHECK(vs::prepare(zoh) == VS_ERR_UNSUPPORTED);
+    vs::Call longer = c;
+    longer.batch = longer.dim = 1;
+    longer.L = (int64_t(1) << 26) + 1;
+    CHECK(vs::prepare(longer) == VS_ERR_UNSUPPORTED);
 }
 
 void proj_validation() {

@@ -69,10 +69,8 @@ def test_cross_scan_in_a_graph():
 
 
 def test_gradient_in_a_graph():
-    """The gradient's launches include fill kernels that zero its summed
-    outputs; they are kernels, not memset nodes. dA, dD and ddt_bias are
-    summed with atomics in any order, so the bitwise check covers the
-    per-token outputs and the fixed-order dB, dC sums."""
+    """The gradient's three kernels; every output, the fixed-order sums
+    included, must repeat bit for bit."""
     import vision_mamba_selective_amd as vms
     wl = wlm.WORKLOADS[1].with_(batch=2, dim=24, seqlen=70)
     inp = wlm.make_inputs(wl, random_A=True, random_D=True)
@@ -86,12 +84,42 @@ def test_gradient_in_a_graph():
         g = vms.vim_scan_bidir_grad(t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"],
                                     t["dt_bias"], dy, workspace=ws)
         return torch.cat([g["du"].float().flatten(), g["ddelta"].float().flatten(),
-                          g["dz"].float().flatten(), g["dB"].flatten(), g["dC"].flatten()])
+                          g["dz"].float().flatten(), g["dB"].flatten(), g["dC"].flatten(),
+                          g["dA"].flatten(), g["dD"].flatten(), g["ddt_bias"].flatten()])
 
     eager = run().clone()
     torch.cuda.synchronize()
     say("case graph gradient")
     replay_and_check(run, eager, "vim_scan_bidir_grad")
+
+
+def test_training_pair_in_a_graph():
+    """The saving forward and the saved-state gradient captured as one graph
+    (a training step of the scan): y and every gradient repeat bit for bit."""
+    import vision_mamba_selective_amd as vms
+    wl = wlm.WORKLOADS[1].with_(batch=2, dim=24, seqlen=150)
+    inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+    t = upload(inp)
+    dy = torch.from_numpy(wlm.round_bf16(np.random.default_rng(6).standard_normal(inp.u.shape)
+                                         .astype(np.float32))).cuda().to(torch.bfloat16)
+    saved = torch.empty(vms.workspace_bytes(4, wl.batch, wl.dim, wl.seqlen, torch.bfloat16),
+                        dtype=torch.uint8, device="cuda")
+    ws = torch.empty(vms.workspace_bytes(5, wl.batch, wl.dim, wl.seqlen, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(t["u"])
+    args = (t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"], t["dt_bias"])
+
+    def run():
+        vms.vim_scan_bidir_fwd_saved(*args, out=y, saved=saved)
+        g = vms.vim_scan_bidir_grad_saved(*args, saved, dy, workspace=ws)
+        return torch.cat([y.float().flatten(), g["du"].float().flatten(), g["ddelta"].float().flatten(),
+                          g["dz"].float().flatten(), g["dB"].flatten(), g["dC"].flatten(),
+                          g["dA"].flatten(), g["dD"].flatten(), g["ddt_bias"].flatten()])
+
+    eager = run().clone()
+    torch.cuda.synchronize()
+    say("case graph training pair")
+    replay_and_check(run, eager, "vim_scan_bidir_fwd_saved + vim_scan_bidir_grad_saved")
 
 
 def test_out_proj_in_a_graph():
