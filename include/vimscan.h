@@ -99,7 +99,9 @@ enum { VS_OP_VIM_BIDIR = 0, VS_OP_CROSS4 = 1, VS_OP_1D = 2, VS_OP_VIM_GRAD = 3,
  * one for VS_OP_VIM_BIDIR and two for VS_OP_CROSS4 (one per pair of opposite
  * directions); an fp32 y serves as the first, so fp32 needs one fewer.
  * VS_OP_CROSS4 also holds column-major copies of u and delta (2 E elements
- * of the input dtype). VS_OP_1D needs none. Returns 0 for invalid
+ * of the input dtype) when the grid is too large to stage on chip: grids of
+ * up to 256 tokens (fp32) or 512 (bf16) are copied to LDS by the scan
+ * itself and need no copies. VS_OP_1D needs none. Returns 0 for invalid
  * arguments and for batch*dim*seqlen of 2^30 or more, which every entry
  * point refuses (VS_ERR_UNSUPPORTED). */
 size_t vs_workspace_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dtype);

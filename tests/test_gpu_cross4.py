@@ -171,3 +171,34 @@ def test_cross4_scan_only_strict_full_size():
     err, rms = strict_err(y, ref, wl.dtype)
     say("  max |dy| / rms = %.3g (rms %.3g)" % (err, rms))
     assert err <= strict_bound(wl.dtype, wl.seqlen)
+
+
+# Grids whose u and delta fit the LDS budget (8 KB for a workgroup's 4
+# channels: fp32 up to 256 tokens, bf16 up to 512) are staged there in
+# column-major order; larger ones read transposed copies from the workspace.
+# Both sides of the limit, with H != W and channel counts that leave idle
+# channels in the last workgroup.
+GRID_EDGE = [
+    # dtype base, H, W, dim
+    ("f32", 16, 16, 5),      # 256 tokens: the largest fp32 grid in LDS
+    ("f32", 11, 24, 6),      # 264: transposed copies
+    ("f32", 7, 7, 7),        # a VMamba stage grid
+    ("bf16", 16, 32, 5),     # 512 tokens: the largest bf16 grid in LDS
+    ("bf16", 19, 27, 3),     # 513: transposed copies
+    ("bf16", 14, 14, 9),     # a VMamba stage grid
+]
+
+
+@pytest.mark.parametrize("case", GRID_EDGE, ids=["%s-%dx%d" % c[:3] for c in GRID_EDGE])
+def test_cross4_either_side_of_the_lds_grid_limit(case):
+    import vision_mamba_selective_amd as vms
+    name, H, W, d = case
+    base = X4_F32 if name == "f32" else X4_BF16
+    inp = make(base, 2, d, H, W, gate=True, seed=H * W + d, random_A=True, random_D=True)
+    tdt = torch.float32 if name == "f32" else torch.bfloat16
+    es = 4 if name == "f32" else 2
+    in_lds = 2 * 4 * H * W * es <= 8 * 1024
+    e = 2 * d * H * W
+    bufs = (1 if name == "f32" else 2) * e * 4
+    assert vms.workspace_bytes(1, 2, d, H * W, tdt) == bufs + (0 if in_lds else 2 * e * es)
+    check(inp, "grid edge %s %dx%d (%s)" % (name, H, W, "LDS" if in_lds else "copies"))

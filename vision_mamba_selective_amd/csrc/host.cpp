@@ -63,11 +63,12 @@ size_t scan_ws_bytes(int op, int64_t batch, int64_t dim, int64_t seqlen, int dty
     if (op != VS_OP_VIM_BIDIR && op != VS_OP_CROSS4 && op != VS_OP_1D) return 0;
     // fp32 merge buffers of batch*dim*seqlen floats: Vim needs one, the
     // cross-scan two; an fp32 y serves as the first. The cross-scan also
-    // keeps column-major copies of u and delta (input dtype).
+    // keeps column-major copies of u and delta (input dtype) when the grid
+    // is too large to stage in LDS.
     const int64_t elems = batch * dim * seqlen;
     const int64_t bufs = (op == VS_OP_VIM_BIDIR ? 1 : (op == VS_OP_CROSS4 ? 2 : 0)) -
                          (dtype == VS_F32 ? 1 : 0);
-    const int64_t copies = op == VS_OP_CROSS4 ? 2 : 0;
+    const int64_t copies = (op == VS_OP_CROSS4 && !cross4_grid_in_lds(seqlen, dtype)) ? 2 : 0;
     const int64_t es = dtype == VS_BF16 ? 2 : 4;
     if (bufs <= 0 && copies == 0) return 0;
     return static_cast<size_t>(elems * (4 * (bufs > 0 ? bufs : 0) + es * copies));

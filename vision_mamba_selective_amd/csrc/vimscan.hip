@@ -288,9 +288,14 @@ struct Unroll<0> {
 //   last chunk     : the prefix, split: row 1 the part from token 0, row 0
 //                    the rest, which then combines both.
 template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false,
-          bool ZOH = false, bool CHUNK = false>
+          bool ZOH = false, bool CHUNK = false, bool GLDS = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
+    // GLDS (cross-scan grids that fit, vs::cross4_grid_in_lds): the
+    // workgroup copies its channels' u and delta into LDS in column-major
+    // order, and the column-major orders read them there instead of from
+    // transposed copies in the workspace
+    static_assert(!GLDS || MODE == kModeCross4, "the LDS grid serves the cross-scan's column orders");
     static_assert(!CHUNK || (MODE == kModeVim && !CONV && !CKPT && !ZOH),
                   "chunks: the plain Vim scan only");
     // CKPT (the gradient's forward pass): store every row's state at each
@@ -302,6 +307,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!(ZOH && CKPT), "the gradient uses delta B");
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
+    static_assert(MODE != kModeCross4 || kChPerWg == vs::kCrossChPerWg, "the host sizes the LDS grid");
     constexpr int kSides = kDirs;              // one B/C tile per direction
     // B/C tiles of kPairTok tokens (two blocks; measured faster than four
     // for short and long sequences alike), rows padded to kPairPad floats,
@@ -660,6 +666,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // be re-masked where the loop carries it, which waits for its load
     using Raw = std::conditional_t<sizeof(T) == 2, uint16_t, uint32_t>;
     struct Tok { Raw u, dl, z, ul, ur; int p; };
+    // the LDS grid (GLDS): [u | delta][channel][column-major token], sized at
+    // launch (2 x kChPerWg x L entries)
+    extern __shared__ __attribute__((aligned(16))) char glds_bytes[];
+    Raw* const glds = reinterpret_cast<Raw*>(glds_bytes);
     auto tok_load = [&](int blk, Tok& k) VS_INLINE {
         if constexpr (kRun) {
             // p holds the token's byte offset within the wave's rows
@@ -672,6 +682,13 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
         const int p = tok_pos(blk);
         k.p = p;
+        if constexpr (GLDS) {
+            if (colpair) {          // uniform per wave
+                k.u = glds[ch * Lseq + p];
+                k.dl = glds[(kChPerWg + ch) * Lseq + p];
+                return;
+            }
+        }
         k.u = act_row(ub, u_row, p);
         if (CONV) {   // the neighbours (clamped; masked where they fall outside)
             k.ul = act_row(ub, u_row, p > 0 ? p - 1 : 0);
@@ -839,6 +856,25 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
     }
 
+    if constexpr (GLDS) {
+        // the workgroup's u and delta grids, read row by row (coalesced) and
+        // written at their column-major index j H + i; a channel past dim
+        // gets zeros
+        const int Hg = a.H, Wg = a.W;
+        const Raw* __restrict__ ug = static_cast<const Raw*>(a.u);
+        const Raw* __restrict__ dg = static_cast<const Raw*>(a.delta);
+        const int64_t dfirst = static_cast<int64_t>(cg) * kChPerWg;
+        for (int e = tid; e < kChPerWg * Lseq; e += kThreads) {
+            const int c = e / Lseq, r = e - c * Lseq;
+            const int i = r / Wg, j = r - i * Wg;
+            const bool okc = dfirst + c < a.dim;
+            const size_t g = static_cast<size_t>(b * a.dim + (okc ? dfirst + c : 0)) * Lseq + r;
+            const Raw uv = okc ? ug[g] : Raw(0), dv = okc ? dg[g] : Raw(0);
+            glds[c * Lseq + j * Hg + i] = uv;
+            glds[(kChPerWg + c) * Lseq + j * Hg + i] = dv;
+        }
+        wg_barrier();
+    }
     load_tail();
     stage_load(0, sr);
     stage_store(0, sr);
@@ -1639,6 +1675,22 @@ void launch_scan(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanA
         hipLaunchKernelGGL((rowscan_kernel<T, MODE, false, false, CONV, false, ZOH>), grid, blk, 0, st, a);
 }
 
+// the cross-scan with its u and delta grids staged in LDS (lds bytes of
+// dynamic LDS)
+template <typename T, bool ZOH>
+void launch_cross4_lds(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a, size_t lds) {
+    constexpr int M = kModeCross4;
+    const unsigned sh = static_cast<unsigned>(lds);
+    if (c.z && c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, M, true, true, false, false, ZOH, false, true>), grid, blk, sh, st, a);
+    else if (c.z)
+        hipLaunchKernelGGL((rowscan_kernel<T, M, true, false, false, false, ZOH, false, true>), grid, blk, sh, st, a);
+    else if (c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, M, false, true, false, false, ZOH, false, true>), grid, blk, sh, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, M, false, false, false, false, ZOH, false, true>), grid, blk, sh, st, a);
+}
+
 template <typename T, int MODE>
 int launch_t(const Call& c) {
     ScanArgs a{};
@@ -1654,12 +1706,16 @@ int launch_t(const Call& c) {
     a.partial = c.dtype == VS_F32 ? static_cast<float*>(c.y) : ws;
     a.partial2 = nullptr;
     a.uT = a.deltaT = nullptr;
+    const bool grid_lds = MODE == kModeCross4 && vs::cross4_grid_in_lds(c.L, c.dtype);
     if (MODE == kModeCross4) {
-        // workspace: [bf16 only: pair-0 sums][pair-1 sums][u^T][delta^T]
+        // workspace: [bf16 only: pair-0 sums][pair-1 sums][u^T][delta^T],
+        // the transposed copies only for grids too large for LDS
         a.partial2 = c.dtype == VS_F32 ? ws : ws + elems;
-        T* act = reinterpret_cast<T*>(a.partial2 + elems);
-        a.uT = act;
-        a.deltaT = act + elems;
+        if (!grid_lds) {
+            T* act = reinterpret_cast<T*>(a.partial2 + elems);
+            a.uT = act;
+            a.deltaT = act + elems;
+        }
     }
     a.dim = c.dim; a.L = c.L; a.H = c.H; a.W = c.W;
     a.dstate = static_cast<int>(c.dstate);
@@ -1671,7 +1727,7 @@ int launch_t(const Call& c) {
               static_cast<unsigned>(c.batch));
     hipStream_t st = static_cast<hipStream_t>(c.stream);
     const dim3 blk(kThreads);
-    if (MODE == kModeCross4) {
+    if (MODE == kModeCross4 && !grid_lds) {
         const int64_t rows = c.batch * c.dim;
         const unsigned tiles = static_cast<unsigned>(((c.H + kTr - 1) / kTr) * ((c.W + kTr - 1) / kTr));
         const unsigned gy = static_cast<unsigned>(rows < 65535 ? rows : 65535);
@@ -1697,6 +1753,10 @@ int launch_t(const Call& c) {
         } else {
             launch_scan<T, MODE, false, false>(c, grid, blk, st, a);
         }
+    } else if (grid_lds) {
+        const size_t lds = static_cast<size_t>(2 * vs::kCrossChPerWg * c.L) * sizeof(T);
+        if (c.zoh) launch_cross4_lds<T, true>(c, grid, blk, st, a, lds);
+        else launch_cross4_lds<T, false>(c, grid, blk, st, a, lds);
     } else if (c.zoh) {
         launch_scan<T, MODE, false, true>(c, grid, blk, st, a);
     } else {

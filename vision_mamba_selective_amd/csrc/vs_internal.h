@@ -23,6 +23,17 @@ constexpr int64_t kGradMaxL = int64_t(1) << 26;   // gradient descriptors span 2
 
 enum Mode { kMode1D = 0, kModeVim = 1, kModeCross4 = 2 };
 
+constexpr int kCrossChPerWg = 4;             // cross-scan: channels per workgroup
+constexpr int64_t kGridLdsBytes = 8 << 10;   // cross-scan: LDS for the column orders' u and delta
+// The cross-scan stages a workgroup's u and delta grids in LDS, in
+// column-major order, when they take at most kGridLdsBytes (kCrossChPerWg
+// channels x 2 tensors x L entries: fp32 grids up to 256 tokens, bf16 up to
+// 512). Beyond that the LDS costs workgroups per CU (the B/C tiles already
+// take 36 KB) and the transposed copies in the workspace are faster.
+inline bool cross4_grid_in_lds(int64_t L, int dtype) {
+    return L >= 1 && 2 * kCrossChPerWg * L * (dtype == VS_BF16 ? 2 : 4) <= kGridLdsBytes;
+}
+
 // One forward scan call (every scan entry point but the gradient).
 struct Call {
     int mode;
