@@ -10,8 +10,10 @@
 // Mapping onto CDNA4 (one recurrence = one (batch, channel, direction)):
 //   * A 16-lane DPP row holds one recurrence; lane n holds state n in a VGPR.
 //     A wave64 therefore runs 4 recurrences, which gives the launch
-//     batch*dim*ndir*16 lanes: enough waves to fill 256 CUs even at batch 2-8,
-//     without splitting the sequence (which would repeat the exp work).
+//     batch*dim*ndir*16 lanes: enough waves to fill 256 CUs at batch 2-8 for
+//     most shapes. Grids that leave SIMDs idle split the sequence into
+//     chunks joined by the associative carry combine (the CHUNK form), at
+//     the cost of a first pass over the other chunks' tokens.
 //   * Tokens are processed in blocks of 16. Lane j of a row loads token j of
 //     the block (coalesced within the row), computes its delta = softplus(.)
 //     and delta*u once, and the row broadcasts them to every state lane with
@@ -22,7 +24,9 @@
 //   * The read-out sum over states (y = C . h) is a 16-lane transpose
 //     reduction inside the row after each block: lane j ends with token j.
 //   * Reverse orders are index arithmetic on the token address; nothing is
-//     flipped in memory. The VMamba column-major pair reads u and delta from
+//     flipped in memory. The VMamba column-major pair reads u and delta by
+//     their column-major index: from an LDS copy that the workgroup writes
+//     in that order when the grid fits (the GLDS form), otherwise from
 //     column-major copies that a transpose pre-pass writes to the workspace
 //     (strided reads of the row-major grid measured 2.5x slower).
 //   * Directions that visit a token at different times meet through an fp32
