@@ -2,7 +2,9 @@
 oracle element by element through the C ABI: sequence lengths around the
 16-token blocks and 32-token tiles, channel counts that leave workgroups
 partly idle, d_state from 1 to 16, H != W grids for the cross-scan, bf16 and
-fp32, with and without the gate and the exact hold, and the gradient."""
+fp32, with and without the gate and the exact hold, the gradient, and the
+training pair (the saving forward's y and the gradient from its saved
+states)."""
 import numpy as np
 import pytest
 
@@ -16,7 +18,7 @@ from vision_mamba_selective_amd import workloads as wlm
 pytestmark = pytest.mark.gpu
 
 BASES = [wlm.WORKLOADS[0], wlm.WORKLOADS[1]]
-NCASE = 70
+NCASE = 80
 
 
 @pytest.mark.parametrize("case", range(NCASE))
@@ -31,13 +33,13 @@ def test_random_shape(case):
             return max(1, 16 * k + int(rng.integers(-2, 3)))
         return int(rng.integers(1, 400))
 
-    kind = ["vim", "vim", "cross4", "1d", "conv", "dirs", "grad"][case % 7]
+    kind = ["vim", "vim", "cross4", "1d", "conv", "dirs", "grad", "saved"][case % 8]
     base = BASES[int(rng.integers(0, 2))]
     b = int(rng.integers(1, 4))
     d = int(rng.integers(1, 41))
     N = int(rng.choice([1, 4, 8, 12, 15, 16, 16, 16]))
     gate = bool(rng.random() < 0.7)
-    zoh = bool(rng.random() < 0.25) and kind not in ("grad",)
+    zoh = bool(rng.random() < 0.25) and kind not in ("grad", "saved")
     seed = int(rng.integers(0, 1 << 30))
     if kind == "cross4":
         H, W = int(rng.integers(1, 41)), int(rng.integers(1, 41))
@@ -82,9 +84,19 @@ def test_random_shape(case):
         x = td.dir_inputs(wl)
         y = gu.host64(td.run(wl, x))
         gu.assert_close(y, td.reference(x), wl.dtype, tag)
-    else:
+    elif kind == "grad":
         inp = wlm.make_inputs(wl, random_A=True, random_D=True)
         dy = tg.upstream(inp, seed=seed % 1000)
         got = tg.run_grad(inp, dy)
+        ref = oracle.vim_bidir_grad(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias, dy)
+        tg.compare(got, ref, wl.dtype, tag)
+    else:
+        inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+        dy = tg.upstream(inp, seed=seed % 1000)
+        t = gu.upload(inp)
+        args = (t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"], t["dt_bias"])
+        y, saved = vms.vim_scan_bidir_fwd_saved(*args)
+        got = vms.vim_scan_bidir_grad_saved(*args, saved, gu.dev(dy, gu.torch_dtype(wl)))
+        gu.assert_close(gu.host64(y), oracle.run_inputs(inp), wl.dtype, tag + " y")
         ref = oracle.vim_bidir_grad(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias, dy)
         tg.compare(got, ref, wl.dtype, tag)
