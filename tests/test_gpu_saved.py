@@ -136,3 +136,40 @@ def test_vim_s_1024_saved_pair():
     same_bits(g_s, g_p, "vim_s_1024")
     for k in PER_TOKEN + SUMMED:
         assert torch.isfinite(g_s[k].float()).all(), k
+
+
+@pytest.mark.parametrize("gate", [True, False], ids=["gated", "plain"])
+@pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
+def test_autograd_function(base, gate):
+    """VimScanFunction: y.backward(dy) leaves the saved-state gradient in
+    every input's .grad (B and C in their dtype), the same bits as the
+    library calls, and the oracle's gradient to the gradient tolerances."""
+    import vision_mamba_selective_amd as vms
+    wl = base.with_(batch=2, dim=10, seqlen=150, gate=gate, seed=321 + gate)
+    inp = wlm.make_inputs(wl, random_A=True, random_D=True)
+    dy = upstream(inp, seed=17)
+    t = upload(inp)
+    leaves = {k: (v.clone().requires_grad_(True) if v is not None else None) for k, v in t.items()}
+    say("case autograd %s gate=%s" % (wl.dtype, gate))
+    y = vms.vim_scan_bidir_autograd(leaves["u"], leaves["delta"], leaves["z"], leaves["B"], leaves["C"],
+                                    leaves["A"], leaves["Dskip"], leaves["dt_bias"])
+    dy_t = dev(dy, torch_dtype(wl))
+    y.backward(dy_t)
+    args = (t["u"], t["delta"], t["z"], t["B"], t["C"], t["A"], t["Dskip"], t["dt_bias"])
+    y_p, saved = vms.vim_scan_bidir_fwd_saved(*args)
+    g = vms.vim_scan_bidir_grad_saved(*args, saved, dy_t)
+    assert torch.equal(y.detach(), y_p)
+    names = {"u": "du", "delta": "ddelta", "z": "dz", "A": "dA", "Dskip": "dD", "dt_bias": "ddt_bias"}
+    for leaf, key in names.items():
+        if leaves[leaf] is None:
+            continue
+        assert torch.equal(leaves[leaf].grad, g[key]), leaf
+    for leaf, key in (("B", "dB"), ("C", "dC")):
+        assert leaves[leaf].grad.dtype == t[leaf].dtype
+        assert torch.equal(leaves[leaf].grad, g[key].to(t[leaf].dtype)), leaf
+    ref = oracle.vim_bidir_grad(inp.u, inp.delta, inp.z, inp.B, inp.C, inp.A, inp.D, inp.dt_bias, dy)
+    got = {names[k]: leaves[k].grad for k in names if leaves[k] is not None}
+    got.update(dB=g["dB"], dC=g["dC"])
+    if not gate:
+        got["dz"] = None
+    compare(got, ref, wl.dtype, "autograd")

@@ -9,6 +9,7 @@ library.
 
 __all__ = ["vim_scan_bidir", "vim_scan_bidir_noalloc", "vim_scan_bidir_chunked", "vim_scan_bidir_dirs", "vim_scan_bidir_conv", "vim_scan_bidir_grad",
            "vim_scan_bidir_fwd_saved", "vim_scan_bidir_grad_saved",
+           "VimScanFunction", "vim_scan_bidir_autograd",
            "vmamba_cross_scan4", "s6_scan_1d", "workspace_bytes", "vim_x_proj", "vim_dt_proj",
            "vim_out_proj"]
 

@@ -439,3 +439,33 @@ def vim_out_proj(y, W, bias=None, residual=None, out=None):
                               _ptr(bias), _ptr(residual), _ptr(o), _stream(dev))
     nat.check("vim_out_proj", rc)
     return o
+
+
+class VimScanFunction(torch.autograd.Function):
+    """vim_scan_bidir for autograd: the forward runs vim_scan_bidir_fwd_saved
+    and keeps its saved-state buffer for the backward, which runs
+    vim_scan_bidir_grad_saved. The gradients of B and C come back in B's and
+    C's dtype (the library sums them in fp32); Dskip and dt_bias given as
+    None get no gradient."""
+
+    @staticmethod
+    def forward(ctx, u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus=True):
+        y, saved = vim_scan_bidir_fwd_saved(u, delta, z, B, C, A, Dskip, dt_bias,
+                                            delta_softplus=delta_softplus)
+        ctx.save_for_backward(u, delta, z, B, C, A, Dskip, dt_bias, saved)
+        ctx.delta_softplus = delta_softplus
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        u, delta, z, B, C, A, Dskip, dt_bias, saved = ctx.saved_tensors
+        dy = dy.to(u.dtype).contiguous()
+        g = vim_scan_bidir_grad_saved(u, delta, z, B, C, A, Dskip, dt_bias, saved, dy,
+                                      delta_softplus=ctx.delta_softplus)
+        return (g["du"], g["ddelta"], g["dz"], g["dB"].to(B.dtype), g["dC"].to(C.dtype), g["dA"],
+                None if Dskip is None else g["dD"], None if dt_bias is None else g["ddt_bias"], None)
+
+
+def vim_scan_bidir_autograd(u, delta, z, B, C, A, Dskip=None, dt_bias=None, delta_softplus=True):
+    """vim_scan_bidir as a differentiable op (VimScanFunction)."""
+    return VimScanFunction.apply(u, delta, z, B, C, A, Dskip, dt_bias, delta_softplus)
