@@ -767,13 +767,16 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int lmax = pl0 > pl1 ? pl0 : pl1;
         const int nblk_a = (lmax + kBlockTok - 1) / kBlockTok;
         const int npair_a = (nblk_a + kBpt - 1) / kBpt;
+        // the piece's tokens through the wave's descriptors, as the main scan
+        // reads its own: one byte offset per lane, linear in the block and
+        // never clamped (past the piece it reads a token no valid step uses,
+        // or nothing outside the wave's rows)
+        const int oa0 = (lane_rel + mpa + (mrev ? mlen - 1 - n : n)) * static_cast<int>(kEs);
+        const int oa_inc = (mrev ? -kBlockTok : kBlockTok) * static_cast<int>(kEs);
         auto tok_load_a = [&](int blk, Tok& k) VS_INLINE {
-            const int t = blk * kBlockTok + n;
-            const int tc = t < mlen ? t : mlen - 1;
-            const int p = mpa + (mrev ? mlen - 1 - tc : tc);
-            k.p = p;
-            k.u = act_row(ub, u_row, p);
-            k.dl = act_row(db, dl_row, p);
+            const int ob = oa0 + blk * oa_inc;
+            k.u = static_cast<Raw>(rload(rs_u, ob, 0));
+            k.dl = static_cast<Raw>(rload(rs_dl, ob, 0));
         };
         stage_load_any(0, sr, true);
         stage_store(0, sr);
@@ -795,7 +798,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const float cu = from_raw<T>(cur.u);
             const float x = from_raw<T>(cur.dl) + bias_a;
             const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
-            const float du = dlt * cu;
+            // the select keeps a non-finite value read past the piece (it may
+            // be another channel's) out of the state
+            const float du = ok ? dlt * cu : 0.f;
             sdl += dlt;
             const float4* Bt = reinterpret_cast<const float4*>(&tile[buf][pside][0][n][half * kBlockTok]);
             float Bv[16];
