@@ -1142,8 +1142,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 // ---------------------------------------------------------------- gradient
 // Reverse-mode gradient of the Vim scan (vim_scan_bidir_grad). Same row
 // layout as rowscan_kernel (one recurrence per 16-lane row, lane n = state
-// n, 8 channels x {forward, backward} per workgroup) with the blocks taken
-// in reverse order. Per block:
+// n, CH channels x {forward, backward} per workgroup: 24 when that still
+// gives every CU a workgroup, else 8) with the blocks taken in reverse
+// order. Per block:
 //   * the states h_t of the block's 16 steps are recomputed from the state
 //     stored at the block's start by the forward pass (rowscan_kernel with
 //     CKPT), keeping h_t and e_t = exp(delta_t A_n) in registers;
@@ -1162,7 +1163,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
 //   * dB and dC are shared by every channel: each lane holds its state's
 //     contributions for the block's 16 steps. A 32-lane swap sums the wave's
 //     two rows of the same direction (dB lands in the low half of the wave,
-//     dC in the high half), LDS sums the four waves, and the workgroup
+//     dC in the high half), LDS sums the workgroup's waves, and the workgroup
 //     stores its 1024 block sums (dB|dC x side x step x state) as one
 //     contiguous 4 KB chunk. grad_bc_reduce_kernel then sums the chunks over
 //     the workgroups in a fixed order, so no atomics are involved and dB and
