@@ -1546,17 +1546,20 @@ void rowgrad_kernel(const GradArgs a) {
 }
 
 // dB and dC from the gradient kernel's chunks: the sum over the workgroups of
-// side 0 at step t = token t and side 1 at step t = token L-1-t. One thread
-// per (state, token) of a 16-token block; the workgroups are added in a fixed
-// order. The workgroups past the nblk blocks of batch row 0 sum dA, dD and
-// dt_bias over the batch rows, in order, one thread per output.
+// side 0 at step t = token t and side 1 at step t = token L-1-t. A thread
+// takes four consecutive states of one token (16-byte loads), a workgroup
+// 64 tokens; the workgroups of the gradient are added in a fixed order. The
+// workgroups past the token range of batch row 0 sum dA, dD and dt_bias over
+// the batch rows, in order, one thread per output.
+constexpr int kRedTok = kThreads / 4;       // tokens per reduction workgroup
 __global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
         const float* __restrict__ part, float* __restrict__ dB, float* __restrict__ dC, int64_t L,
         int dstate, int nblk, int ngroups, const float* __restrict__ pstat, float* __restrict__ dA,
         float* __restrict__ dD, float* __restrict__ dbias, int64_t dim, int batch) {
-    if (static_cast<int>(blockIdx.x) >= nblk) {
+    const int ntb = static_cast<int>((L + kRedTok - 1) / kRedTok);
+    if (static_cast<int>(blockIdx.x) >= ntb) {
         const int64_t np = 2 * dim * (dstate + 2);
-        const int64_t k = static_cast<int64_t>(blockIdx.x - nblk) * kThreads + threadIdx.x;
+        const int64_t k = static_cast<int64_t>(blockIdx.x - ntb) * kThreads + threadIdx.x;
         if (blockIdx.y != 0 || k >= np) return;
         float sum = 0.f;
         for (int b = 0; b < batch; ++b) sum += pstat[static_cast<size_t>(b) * np + k];
@@ -1566,30 +1569,38 @@ __global__ __launch_bounds__(kThreads) void grad_bc_reduce_kernel(
         else dbias[k - na - 2 * dim] = sum;
         return;
     }
-    // consecutive threads take consecutive states, so that each step's 16
-    // states are one contiguous 64-byte read
-    const int n = threadIdx.x & 15, i = threadIdx.x >> 4;
+    const int q = threadIdx.x & 3;              // states 4q .. 4q + 3
     const int64_t b = blockIdx.y;
-    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kBlockTok + i;
-    if (n >= dstate || tok >= L) return;
+    const int64_t tok = static_cast<int64_t>(blockIdx.x) * kRedTok + (threadIdx.x >> 2);
+    if (tok >= L || 4 * q >= dstate) return;
     const int64_t t1 = L - 1 - tok;
     // [which][side][step][n]: side 0 for the forward direction, 1 for the
-    // backward one; every (side, step) row of a chunk is read by the one
-    // workgroup whose tokens it holds
-    const size_t o0 = static_cast<size_t>(blockIdx.x) * kBcChunk + static_cast<size_t>(i) * kRowLanes + n;
+    // backward one; every (side, step) row of a chunk is read by the
+    // threads whose token it holds
+    const size_t o0 = static_cast<size_t>(tok / kBlockTok) * kBcChunk +
+                      static_cast<size_t>(tok % kBlockTok) * kRowLanes + 4 * q;
     const size_t o1 = static_cast<size_t>(t1 / kBlockTok) * kBcChunk +
-                      static_cast<size_t>(kBlockTok + t1 % kBlockTok) * kRowLanes + n;
+                      static_cast<size_t>(kBlockTok + t1 % kBlockTok) * kRowLanes + 4 * q;
     constexpr size_t kC = kBcChunk / 2;
     const size_t gstride = static_cast<size_t>(nblk) * kBcChunk;
     const float* c = part + static_cast<size_t>(b) * ngroups * gstride;
-    float sB = 0.f, sC = 0.f;
+    float4 sB = make_float4(0.f, 0.f, 0.f, 0.f), sC = sB;
+    auto add2 = [](float4& s, const float4 x, const float4 y) {
+        s.x += x.x + y.x; s.y += x.y + y.y; s.z += x.z + y.z; s.w += x.w + y.w;
+    };
     for (int g = 0; g < ngroups; ++g, c += gstride) {
-        sB += c[o0] + c[o1];
-        sC += c[o0 + kC] + c[o1 + kC];
+        add2(sB, *reinterpret_cast<const float4*>(c + o0), *reinterpret_cast<const float4*>(c + o1));
+        add2(sC, *reinterpret_cast<const float4*>(c + o0 + kC), *reinterpret_cast<const float4*>(c + o1 + kC));
     }
-    const size_t o = static_cast<size_t>(b * dstate + n) * static_cast<size_t>(L) + static_cast<size_t>(tok);
-    dB[o] = sB;
-    dC[o] = sC;
+    const float vb[4] = {sB.x, sB.y, sB.z, sB.w}, vc[4] = {sC.x, sC.y, sC.z, sC.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (4 * q + k >= dstate) break;
+        const size_t o = static_cast<size_t>(b * dstate + 4 * q + k) * static_cast<size_t>(L) +
+                         static_cast<size_t>(tok);
+        dB[o] = vb[k];
+        dC[o] = vc[k];
+    }
 }
 
 // Transpose u and delta of every (batch, channel) from the row-major H x W
@@ -1878,8 +1889,9 @@ int launch_grad(const GradCall& g) {
         launch_rowgrad<T, 8>(g.z != nullptr, g.softplus != 0, grid, st, r);
     // 3. dB and dC; dA, dD and dt_bias
     const int64_t pblocks = (2 * g.dim * (g.dstate + 2) + kThreads - 1) / kThreads;
+    const int64_t ntb = (g.L + kRedTok - 1) / kRedTok;
     hipLaunchKernelGGL(grad_bc_reduce_kernel,
-                       dim3(static_cast<unsigned>(nblk + pblocks), static_cast<unsigned>(g.batch)), blk, 0, st,
+                       dim3(static_cast<unsigned>(ntb + pblocks), static_cast<unsigned>(g.batch)), blk, 0, st,
                        r.bc_part, g.dB, g.dC, g.L, static_cast<int>(g.dstate), nblk, static_cast<int>(groups),
                        r.pstat, g.dA, g.dD, g.dbias, g.dim, static_cast<int>(g.batch));
     hipError_t e = hipGetLastError();
