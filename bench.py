@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--sets", type=int, default=0,
                    help="input sets rotated over the steps (0: enough to exceed 768 MB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="the CPU baseline repeats its sample until this many seconds have passed")
     p.add_argument("--cpu-channels", type=int, default=0,
                    help="channels per batch row in the CPU sample (0: whole workload)")
     p.add_argument("--conv", action="store_true",
@@ -402,12 +404,16 @@ def main():
             conv = (base["cw"].cpu().numpy(), base["cb"].cpu().numpy())
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_channels, conv,
                                            base["dy"].float().cpu().numpy() if backward else None,
-                                           zoh=args.zoh, dirs=args.dirs, train=args.train)
+                                           zoh=args.zoh, dirs=args.dirs, train=args.train,
+                                           min_seconds=args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False, train=False):
-    """The fp64 oracle, as it stands, on the host cores of this machine."""
+def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False, train=False,
+                 min_seconds=10.0):
+    """The fp64 oracle, as it stands, on the host cores of this machine: the
+    sample is run again until min_seconds have passed (at least once), and
+    the rate is the work of all runs over their total time."""
     import numpy as np
     import oracle
     from vision_mamba_selective_amd import workloads as wlm
@@ -421,9 +427,37 @@ def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False, train=
     print("bench: cpu baseline on %s with %d threads" % (desc, threads), file=sys.stderr,
           flush=True)
     oracle.load()
-    t0 = time.perf_counter()
-    if train:       # the forward, then the gradient
+    if train:
         desc += ", forward then gradient"
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        run_oracle_once(wl, sample, nch, conv, dy, zoh, dirs, train, threads)
+        runs += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(runs * sample.wl.tokens_channels / dt / 1e9, 5), "unit": "Gtoken*ch/s",
+            "cores": threads, "kind": "oracle", "seconds": round(dt, 3), "runs": runs,
+            "sample": "%s, %d run%s, fp64, %s, %s" % (desc, runs, "" if runs == 1 else "s", cpu,
+                                                      platform.machine())}
+
+
+def run_oracle_once(wl, sample, nch, conv, dy, zoh, dirs, train, threads):
+    """One pass of the oracle over the sample (the call the bench times)."""
+    import numpy as np
+    import oracle
+    from vision_mamba_selective_amd import workloads as wlm
+    if train:       # the forward, then the gradient
         oracle.run_inputs(sample, nthreads=threads)
     if dy is not None:
         gy = dy[:sample.wl.batch, :sample.wl.dim]
@@ -445,19 +479,6 @@ def cpu_baseline(wl, inp, nch, conv=None, dy=None, zoh=False, dirs=False, train=
         ch = list(range(sample.wl.dim))
         oracle.vim_conv(sample.u, w[:, ch], b[:, ch], sample.delta, sample.z, sample.B, sample.C,
                         sample.A, sample.D, sample.dt_bias, nthreads=threads, zoh=zoh)
-    dt = time.perf_counter() - t0
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    return {"value": round(sample.wl.tokens_channels / dt / 1e9, 5), "unit": "Gtoken*ch/s",
-            "cores": threads, "kind": "oracle", "seconds": round(dt, 3),
-            "sample": desc + ", fp64, " + cpu + ", " + platform.machine()}
 
 
 def proj_bench(args, torch, dev):
