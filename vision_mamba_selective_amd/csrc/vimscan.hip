@@ -80,8 +80,7 @@ struct ScanArgs {
     // Vim with per-direction inputs: the backward rows read u and delta this
     // many elements past the forward rows' (0: shared), and B, C are
     // [batch][2][dstate][L] in token order when bc_per_dir is set
-    uint32_t u_dir_off;
-    uint32_t dl_dir_off;
+    uint32_t dir_off;
     int bc_per_dir;
     int64_t dim;
     int64_t L;
@@ -405,8 +404,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto act_at = [&](const char* base, int p) {
         return ld_raw(reinterpret_cast<const T*>(base + (rowoff + static_cast<uint32_t>(p)) * kEs), 0);
     };
-    const uint32_t u_row = rowoff + (MODE == kModeVim && rev ? a.u_dir_off : 0u);
-    const uint32_t dl_row = rowoff + (MODE == kModeVim && rev ? a.dl_dir_off : 0u);
+    const uint32_t u_row = rowoff + (MODE == kModeVim && rev ? a.dir_off : 0u);
+    const uint32_t dl_row = u_row;
     auto act_row = [&](const char* base, uint32_t row, int p) {
         return ld_raw(reinterpret_cast<const T*>(base + (row + static_cast<uint32_t>(p)) * kEs), 0);
     };
@@ -436,8 +435,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const_cast<char*>(static_cast<const char*>(base)) + wave_base * es, 0,
             static_cast<int>((wave_el + extra_el) * es), 0x00020000);
     };
-    const __amdgpu_buffer_rsrc_t rs_u = wave_rsrc(a.u, kEs, a.u_dir_off);
-    const __amdgpu_buffer_rsrc_t rs_dl = wave_rsrc(a.delta, kEs, a.dl_dir_off);
+    const __amdgpu_buffer_rsrc_t rs_u = wave_rsrc(a.u, kEs, a.dir_off);
+    const __amdgpu_buffer_rsrc_t rs_dl = wave_rsrc(a.delta, kEs, a.dir_off);
     const __amdgpu_buffer_rsrc_t rs_z = wave_rsrc(GATE ? a.z : a.u, kEs, 0u);
     // a checkpointing pass without y gets a descriptor that covers nothing:
     // its y stores are dropped
@@ -451,8 +450,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const int lane_rel = static_cast<int>((d0 - wave_d0) * a.L);
     const int ob0 = (lane_rel + tok0 + (rev ? L - 1 - n : n)) * static_cast<int>(kEs);
     const int ob_inc = (rev ? -kBlockTok : kBlockTok) * static_cast<int>(kEs);
-    const int ou_lane = rev ? static_cast<int>(a.u_dir_off * kEs) : 0;
-    const int od_lane = rev ? static_cast<int>(a.dl_dir_off * kEs) : 0;
+    // u and delta of a backward row (per-direction inputs)
+    const int o_dir = rev ? static_cast<int>(a.dir_off * kEs) : 0;
     auto rload = [&](__amdgpu_buffer_rsrc_t r, int off, int soff) VS_INLINE {
         if constexpr (sizeof(T) == 2)
             return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
@@ -473,10 +472,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // bf16 or 4 fp32 entries) that lie contiguously in memory, in token order
     // or, for a side that reads token L-1-t, in reverse order. Thread tid
     // loads chunks tid, tid + 256, ... with one 16-byte load each (rows start
-    // at any 2-byte boundary; the target handles unaligned global loads). A
-    // last tile that the sequence does not fill is read entry by entry,
-    // clamped, once before the loop (nothing else in flight then) and kept
-    // in registers until its turn. Vim's two sides read the shared B/C at tokens t and L-1-t;
+    // at any 2-byte boundary; the target handles unaligned global loads), at
+    // a per-lane offset that steps by one tile per tile. A last tile that
+    // the sequence does not fill is read entry by entry, clamped, when its
+    // turn comes. Vim's two sides read the shared B/C at tokens t and L-1-t;
     // each cross-scan direction reads its own B/C, stored in its scan order.
     //
     // The store builds each fp32 tile entry with one byte permute (v_perm)
@@ -516,6 +515,9 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     bool cok[kCpt];             // the chunk's state row is < dstate
     int cdst[kCpt];             // tile_mem index of the chunk in buffer 0
     int ctok0[kCpt], clen[kCpt];    // the side's token range (uniform per wave)
+    // byte offset of the chunk's 16 bytes in tile 0, and its step per tile
+    // (negative in reverse order; uniform per wave)
+    int cbase[kCpt], cinc[kCpt];
     // A side s reads tokens [sd_tok0[s], sd_tok0[s] + sd_len[s]) in token
     // order, or from the top down when sd_rev[s]; with_c = false stages B only.
     auto stage_setup = [&](const int (&sd_tok0)[kSides], const int (&sd_len)[kSides],
@@ -545,6 +547,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             cselx[j] = !ok_row ? kSelZero : (rv ? kSelRevX : kSelFwdX);
             csely[j] = !ok_row ? kSelZero : (rv ? kSelRevY : kSelFwdY);
             cdst[j] = ((side * 2 + (q & 1)) * kRowLanes + srow) * kPairPad + k * kTpc;
+            const uint32_t first0 = static_cast<uint32_t>(ctok0[j]) +
+                                    (crev[j] ? static_cast<uint32_t>(clen[j] - kTpc - ccol[j])
+                                             : static_cast<uint32_t>(ccol[j]));
+            cbase[j] = static_cast<int>((crow[j] + first0) * kEs);
+            cinc[j] = (crev[j] ? -kPairTok : kPairTok) * static_cast<int>(kEs);
         }
     };
     // The tile `pair` of chunk j's side, entry by entry and clamped into the
@@ -584,41 +591,20 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
         stage_setup(sd_tok0, sd_len, sd_rev, true);
     }
-    const int ntile = (L + kPairTok - 1) / kPairTok;
-    const bool tail_part = ntile * kPairTok > L;                // uniform
-    uint4 tail_raw[kCpt];
-    // the scan's last tile, when the sequence does not fill it, is read once
-    // before the loop (nothing else in flight then) and kept in registers
-    auto load_tail = [&]() VS_INLINE {
-        if (tail_part) {
-#pragma unroll
-            for (int j = 0; j < kCpt; ++j)
-                if (cin[j]) tail_raw[j] = stage_entries(ntile - 1, j);
-        }
-    };
-    // whole tiles with one 16-byte load per chunk; a tile the side's range
-    // does not fill comes from tail_raw (in_loop_tail = false) or is read
-    // entry by entry here
-    auto stage_load_any = [&](int pair, uint4 (&raw)[kCpt], bool in_loop_tail) VS_INLINE {
+    // whole tiles with one 16-byte load per chunk at its running offset; a
+    // last tile that the side's range does not fill is read entry by entry
+    // (once per scan, in a branch that is uniform per wave)
+    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) VS_INLINE {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
             if (!cin[j]) continue;
-            const int t0 = pair * kPairTok + ccol[j];
-            const bool whole = (pair + 1) * kPairTok <= clen[j];      // uniform per wave
-            if (whole) {
-                const uint32_t first = static_cast<uint32_t>(ctok0[j]) +
-                                       (crev[j] ? static_cast<uint32_t>(clen[j] - kTpc - t0)
-                                                : static_cast<uint32_t>(t0));
+            if ((pair + 1) * kPairTok <= clen[j])
                 raw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       csrc[j], static_cast<int>((crow[j] + first) * kEs), 0, 0));
-            } else if (in_loop_tail) {
+                                                       csrc[j], cbase[j] + pair * cinc[j], 0, 0));
+            else
                 raw[j] = stage_entries(pair, j);
-            } else {
-                raw[j] = tail_raw[j];
-            }
         }
     };
-    auto stage_load = [&](int pair, uint4 (&raw)[kCpt]) VS_INLINE { stage_load_any(pair, raw, false); };
     auto stage_store = [&](int buf, const uint4 (&raw)[kCpt]) VS_INLINE {
 #pragma unroll
         for (int j = 0; j < kCpt; ++j) {
@@ -679,8 +665,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             // p holds the token's byte offset within the wave's rows
             const int ob = ob0 + blk * ob_inc;
             k.p = ob;
-            k.u = static_cast<Raw>(rload(rs_u, ob + ou_lane, 0));
-            k.dl = static_cast<Raw>(rload(rs_dl, ob + od_lane, 0));
+            k.u = static_cast<Raw>(rload(rs_u, ob + o_dir, 0));
+            k.dl = static_cast<Raw>(rload(rs_dl, ob + o_dir, 0));
             if (GATE) k.z = static_cast<Raw>(rload(rs_z, ob, blk >= Fstep ? 0 : kOob));
             return;
         }
@@ -778,7 +764,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             k.u = static_cast<Raw>(rload(rs_u, ob, 0));
             k.dl = static_cast<Raw>(rload(rs_dl, ob, 0));
         };
-        stage_load_any(0, sr, true);
+        stage_load(0, sr);
         stage_store(0, sr);
         Unroll<kTokAhead>::run([&](auto ic) {
             constexpr int k = decltype(ic)::value;
@@ -791,10 +777,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const int half = blk % kBpt;
             if (half == 0) {
                 const int pair = blk / kBpt;
-                stage_load_any(pair + 1 < npair_a ? pair + 1 : pair, sr, true);
+                stage_load(pair + 1 < npair_a ? pair + 1 : pair, sr);
             }
             tok_load_a(blk + kTokAhead < nblk_a ? blk + kTokAhead : nblk_a - 1, nxt);
-            const bool ok = active && blk * kBlockTok + n < mpl;
+            const bool ok = active && n < mpl - blk * kBlockTok;
             const float cu = from_raw<T>(cur.u);
             const float x = from_raw<T>(cur.dl) + bias_a;
             const float dlt = ok ? (SOFTPLUS ? softplus_f(x) : x) : 0.f;
@@ -884,7 +870,6 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         }
         wg_barrier();
     }
-    load_tail();
     stage_load(0, sr);
     stage_store(0, sr);
     Unroll<kTokAhead>::run([&](auto ic) {
@@ -912,7 +897,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         const int buf = (blk / kBpt) & 1;
         const int half = blk % kBpt;
         const int p = cur.p;
-        const bool ok = active && blk * kBlockTok + n < L;
+        const bool ok = active && n < L - blk * kBlockTok;
         if constexpr (CKPT)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(h), rs_ck, ck_off0 + blk * (kRowLanes * 4), 0, 0);
         // the other direction's partial sum, for blocks after step F (it was
@@ -1718,7 +1703,7 @@ int launch_t(const Call& c) {
     a.u = c.u; a.delta = c.delta; a.z = c.z; a.B = c.B; a.C = c.C;
     a.A = c.A; a.Dskip = c.Dskip; a.dt_bias = c.dt_bias; a.y = c.y;
     a.conv_w = c.conv_w; a.conv_b = c.conv_b;
-    a.u_dir_off = a.dl_dir_off = c.per_dir ? static_cast<uint32_t>(c.batch * c.dim * c.L) : 0u;
+    a.dir_off = c.per_dir ? static_cast<uint32_t>(c.batch * c.dim * c.L) : 0u;
     a.bc_per_dir = c.per_dir ? 1 : 0;
     // merge buffers: fp32 y doubles as the first one; the cross-scan's second
     // pair always uses the workspace (after the first buffer if y is bf16)
