@@ -91,6 +91,31 @@ def test_vim_delta_zero_is_exact(base):
     assert torch.equal(y, 2 * t["u"])
 
 
+# The forward and backward rows of a channel hand each other their partial
+# sums through LDS when a workgroup's 8 channels x L fp32 entries and two
+# 16-entry guards fit in 8 KB (L <= 252), through global memory beyond.
+PART_EDGE = [(252, "LDS"), (253, "global"), (197, "LDS"), (17, "LDS")]
+
+
+@pytest.mark.parametrize("case", PART_EDGE, ids=["%d-%s" % c for c in PART_EDGE])
+@pytest.mark.parametrize("base", [VIM_F32, VIM_BF16], ids=["f32", "bf16"])
+def test_vim_either_side_of_the_lds_partial_limit(case, base):
+    L, where = case
+    assert (8 * L + 32) * 4 <= 8192 if where == "LDS" else (8 * L + 32) * 4 > 8192
+    wl = base.with_(batch=2, dim=11, seqlen=L, seed=500 + L)
+    check(wlm.make_inputs(wl, random_A=True, random_D=True), "partial sums in %s, L %d" % (where, L))
+    # scan term alone (D = 0, no gate): a partial sum handed to the wrong
+    # token or lane cannot hide under the skip term
+    wl = wl.with_(gate=False)
+    inp = wlm.make_inputs(wl, random_A=True)
+    inp.D[:] = 0.0
+    say("case partial sums in %s, strict, L %d" % (where, L))
+    y = host64(run_gpu(inp))
+    err, rms = strict_err(y, oracle.run_inputs(inp), wl.dtype)
+    say("  max (|dy| - output rounding) / rms = %.3g (rms %.3g)" % (err, rms))
+    assert err <= STRICT[wl.dtype]
+
+
 def test_vim_repeatable_and_in_bounds():
     """Two runs give identical bits; nothing outside y is written."""
     wl = VIM_BF16.with_(batch=3, dim=21, seqlen=111)

@@ -291,7 +291,7 @@ struct Unroll<0> {
 //   last chunk     : the prefix, split: row 1 the part from token 0, row 0
 //                    the rest, which then combines both.
 template <typename T, int MODE, bool GATE, bool SOFTPLUS, bool CONV = false, bool CKPT = false,
-          bool ZOH = false, bool CHUNK = false, bool GLDS = false>
+          bool ZOH = false, bool CHUNK = false, bool GLDS = false, bool PLDS = false>
 __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!CONV || MODE == kModeVim, "the conv front end is Vim's");
     // GLDS (cross-scan grids that fit, vs::cross4_grid_in_lds): the
@@ -299,6 +299,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // order, and the column-major orders read them there instead of from
     // transposed copies in the workspace
     static_assert(!GLDS || MODE == kModeCross4, "the LDS grid serves the cross-scan's column orders");
+    // PLDS (Vim sequences that fit, vs::vim_partial_lds_bytes): a channel's
+    // forward and backward rows, which share a wave, hand each other their
+    // partial sums through dynamic LDS, [channel][token] after a guard,
+    // instead of the fp32 buffer in global memory
+    static_assert(!PLDS || (MODE == kModeVim && !CONV && !CKPT && !ZOH),
+                  "partial sums in LDS: the Vim scan without checkpoints");
     static_assert(!CHUNK || (MODE == kModeVim && !CONV && !CKPT && !ZOH),
                   "chunks: the plain Vim scan only");
     // CKPT (the gradient's forward pass): store every row's state at each
@@ -310,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     static_assert(!(ZOH && CKPT), "the gradient uses delta B");
     constexpr int kDirs = MODE == kModeVim ? 2 : (MODE == kModeCross4 ? 4 : 1);
     constexpr int kChPerWg = 16 / kDirs;
+    static_assert(MODE != kModeVim || kChPerWg == vs::kVimChPerWg, "the host sizes the LDS partial sums");
     static_assert(MODE != kModeCross4 || kChPerWg == vs::kCrossChPerWg, "the host sizes the LDS grid");
     constexpr int kSides = kDirs;              // one B/C tile per direction
     // B/C tiles of kPairTok tokens (two blocks; measured faster than four
@@ -660,6 +667,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // launch (2 x kChPerWg x L entries)
     extern __shared__ __attribute__((aligned(16))) char glds_bytes[];
     Raw* const glds = reinterpret_cast<Raw*>(glds_bytes);
+    // PLDS: byte offset of this lane's token of block blk in the LDS partial
+    // sums, lp0 + blk * lp_inc (past either end of the row it falls in a
+    // guard or a neighbour row, and only stores of valid tokens are made)
+    const int lp0 = (vs::kPartLdsGuard + ch * L + (rev ? L - 1 - n : n)) * 4;
+    const int lp_inc = (rev ? -kBlockTok : kBlockTok) * 4;
+    auto lpart = [&](int blk) { return reinterpret_cast<float*>(glds_bytes + lp0 + blk * lp_inc); };
     auto tok_load = [&](int blk, Tok& k) VS_INLINE {
         if constexpr (kRun) {
             // p holds the token's byte offset within the wave's rows
@@ -905,8 +918,11 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // entry 0 of the row instead (unused) rather than branch. Issued
         // before the prefetch so that waiting for it does not wait for those.
         float part = 0.f;
-        if (kRun)      // agent-coherent (sc1), as the atomic load below
+        if (PLDS) {
+            if (blk > Fstep) part = *lpart(blk);
+        } else if (kRun) {  // agent-coherent (sc1), as the atomic load below
             part = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_p, poff(p), blk > Fstep ? 0 : kOob, 16));
+        }
         else if (MODE != kMode1D)
             part = __hip_atomic_load(part_at(blk > Fstep ? p : 0), __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -982,7 +998,8 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             if (ok) st(y_at(p), 0, yk * gate);
         } else if (blk < Fstep) {
             if (ok) {
-                if (kRun) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yk), rs_p, poff(p), 0, 0);
+                if (PLDS) *lpart(blk) = yk;
+                else if (kRun) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yk), rs_p, poff(p), 0, 0);
                 else *part_at(p) = yk;
             }
         } else if (blk > Fstep) {
@@ -995,12 +1012,19 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const int t_self = blk * kBlockTok + n;
             const int blk_other = (L - 1 - t_self) / kBlockTok;
             const bool first = blk < blk_other || (blk == blk_other && pside == 0);
-            if (ok && first)
-                __hip_atomic_store(part_at(p), yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+            // (PLDS) the token's entry in the LDS partial sums
+            float* const lp = reinterpret_cast<float*>(glds_bytes) + vs::kPartLdsGuard + ch * L + (p - tok0);
+            if (ok && first) {
+                if (PLDS) *lp = yk;
+                else __hip_atomic_store(part_at(p), yk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            // both rows are in this wave: with the sums in LDS, waiting for
+            // its own LDS stores orders them before the reads below
+            if (PLDS) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup", "local");
+            else __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
             if (ok && !first) {
-                const float other = __hip_atomic_load(part_at(p), __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
+                const float other = PLDS ? *lp : __hip_atomic_load(part_at(p), __ATOMIC_RELAXED,
+                                                                   __HIP_MEMORY_SCOPE_AGENT);
                 if (kRun) {
                     // finish through the element pointer as well
                     if (CKPT) *part_at(p) = yk + other;
@@ -1645,6 +1669,22 @@ void launch_chunked(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const Sc
         hipLaunchKernelGGL((rowscan_kernel<T, V, false, false, false, false, false, true>), grid, blk, 0, st, a);
 }
 
+// the Vim scan with its partial sums in LDS (lds bytes of dynamic LDS),
+// chunked or not
+template <typename T, bool CHUNK>
+void launch_vim_plds(const Call& c, dim3 grid, dim3 blk, hipStream_t st, const ScanArgs& a, size_t lds) {
+    constexpr int V = kModeVim;
+    const unsigned sh = static_cast<unsigned>(lds);
+    if (c.z && c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, true, true, false, false, false, CHUNK, false, true>), grid, blk, sh, st, a);
+    else if (c.z)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, true, false, false, false, false, CHUNK, false, true>), grid, blk, sh, st, a);
+    else if (c.softplus)
+        hipLaunchKernelGGL((rowscan_kernel<T, V, false, true, false, false, false, CHUNK, false, true>), grid, blk, sh, st, a);
+    else
+        hipLaunchKernelGGL((rowscan_kernel<T, V, false, false, false, false, false, CHUNK, false, true>), grid, blk, sh, st, a);
+}
+
 // Chunks per sequence for a plain Vim scan. Unchunked, the launch has
 // batch * ceil(dim / 8) workgroups of 4 waves; below 2 waves per SIMD (1,024
 // SIMDs) the chip is under-filled and the sequential length sets the time, so
@@ -1746,11 +1786,21 @@ int launch_t(const Call& c) {
         // the plain scan takes chunks when the grid under-fills the chip
         const bool plain = !c.conv_w && !c.zoh && !c.per_dir;
         const int nchunk = plain ? chunk_count(c) : 1;
+        // the longest chunk (whole 32-token tiles but the last) and whether
+        // its workgroup's partial sums fit in LDS
+        const int64_t ntile = (c.L + vs::kTileTok - 1) / vs::kTileTok;
+        const int64_t lc_tiled = (ntile + nchunk - 1) / nchunk * vs::kTileTok;
+        const int64_t Lc = lc_tiled < c.L ? lc_tiled : c.L;
+        const size_t plds = static_cast<size_t>(vs::vim_partial_lds_bytes(Lc));
+        const bool use_plds = !c.conv_w && !c.zoh && plds <= static_cast<size_t>(vs::kPartLdsBytes);
         if (nchunk > 1) {
             ScanArgs ac = a;
             ac.nchunk = nchunk;
             const dim3 cgrid(grid.x, grid.y * static_cast<unsigned>(nchunk));
-            launch_chunked<T>(c, cgrid, blk, st, ac);
+            if (use_plds) launch_vim_plds<T, true>(c, cgrid, blk, st, ac, plds);
+            else launch_chunked<T>(c, cgrid, blk, st, ac);
+        } else if (use_plds) {
+            launch_vim_plds<T, false>(c, grid, blk, st, a, plds);
         } else if (c.conv_w) {
             if (c.zoh) launch_scan<T, MODE, true, true>(c, grid, blk, st, a);
             else launch_scan<T, MODE, true, false>(c, grid, blk, st, a);

@@ -34,6 +34,16 @@ inline bool cross4_grid_in_lds(int64_t L, int dtype) {
     return L >= 1 && 2 * kCrossChPerWg * L * (dtype == VS_BF16 ? 2 : 4) <= kGridLdsBytes;
 }
 
+constexpr int kVimChPerWg = 8;                // Vim scan: channels per workgroup
+constexpr int kPartLdsGuard = 16;             // Vim: LDS entries before and after the partial sums
+constexpr int64_t kPartLdsBytes = 8 << 10;    // Vim: LDS for the partial sums of short sequences
+// The Vim scan's two directions hand their partial sums to each other
+// through LDS instead of an fp32 buffer in global memory when a workgroup's
+// rows fit in kPartLdsBytes: kVimChPerWg channels x Lc entries (Lc the
+// longest chunk) and a guard of kPartLdsGuard entries at each end, which
+// sequences up to 252 tokens per chunk meet.
+inline int64_t vim_partial_lds_bytes(int64_t Lc) { return (kVimChPerWg * Lc + 2 * kPartLdsGuard) * 4; }
+
 // One forward scan call (every scan entry point but the gradient).
 struct Call {
     int mode;
