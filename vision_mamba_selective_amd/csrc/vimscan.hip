@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     auto y_at = [&](int p) {
         return reinterpret_cast<T*>(yb + (rowoff + static_cast<uint32_t>(p)) * kEs);
     };
-    // Vim token addressing (every form but the conv front end): a wave's two
+    // Vim token addressing (every Vim form): a wave's two
     // channels are adjacent rows of [batch][dim][L], so one buffer descriptor
     // per tensor covers the wave, and a lane's token of block blk is one byte
     // offset ob0 + blk * ob_inc, never clamped: past either end of the
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     // outside the descriptor, where loads return 0. Loads that a block does
     // not need (the gate and the partial sum before the token's second
     // visit) take an out-of-range scalar offset and read nothing.
-    constexpr bool kRun = MODE == kModeVim && !CONV;
+    constexpr bool kRun = MODE == kModeVim;
     constexpr int kOob = 0x40000000;
     const int64_t wave_d0 = static_cast<int64_t>(cg) * kChPerWg + 2 * wave;
     const int64_t wave_left = a.dim - wave_d0;
@@ -459,6 +459,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
     const int ob_inc = (rev ? -kBlockTok : kBlockTok) * static_cast<int>(kEs);
     // u and delta of a backward row (per-direction inputs)
     const int o_dir = rev ? static_cast<int>(a.dir_off * kEs) : 0;
+    // (CONV, never chunked) byte offsets of the sequence's first and last
+    // tokens in this lane's row
+    const int conv_lo = lane_rel * static_cast<int>(kEs);
+    const int conv_hi = (lane_rel + Lseq - 1) * static_cast<int>(kEs);
     auto rload = [&](__amdgpu_buffer_rsrc_t r, int off, int soff) VS_INLINE {
         if constexpr (sizeof(T) == 2)
             return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0));
@@ -679,6 +683,10 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
             const int ob = ob0 + blk * ob_inc;
             k.p = ob;
             k.u = static_cast<Raw>(rload(rs_u, ob + o_dir, 0));
+            if (CONV) {   // the neighbours (masked at the sequence ends)
+                k.ul = static_cast<Raw>(rload(rs_u, ob + o_dir - static_cast<int>(kEs), 0));
+                k.ur = static_cast<Raw>(rload(rs_u, ob + o_dir + static_cast<int>(kEs), 0));
+            }
             k.dl = static_cast<Raw>(rload(rs_dl, ob + o_dir, 0));
             if (GATE) k.z = static_cast<Raw>(rload(rs_z, ob, blk >= Fstep ? 0 : kOob));
             return;
@@ -938,8 +946,12 @@ __global__ __launch_bounds__(kThreads) void rowscan_kernel(const ScanArgs a) {
         // then leave the state unchanged: exp(0) = 1 and no input)
         float cu = from_raw<T>(cur.u);
         if (CONV) {
-            const float xl = p > 0 ? from_raw<T>(cur.ul) : 0.f;
-            const float xr = p < Lseq - 1 ? from_raw<T>(cur.ur) : 0.f;
+            // (kRun: p is the token's byte offset, conv_lo and conv_hi those
+            // of the row's first and last tokens)
+            const bool has_l = kRun ? p > conv_lo : p > 0;
+            const bool has_r = kRun ? p < conv_hi : p < Lseq - 1;
+            const float xl = has_l ? from_raw<T>(cur.ul) : 0.f;
+            const float xr = has_r ? from_raw<T>(cur.ur) : 0.f;
             cu = silu_f(fmaf(cw_l, xl, fmaf(cw_c, cu, fmaf(cw_r, xr, cw_b))));
         }
         const float x = from_raw<T>(cur.dl) + bias;
