@@ -24,8 +24,10 @@
 // work on the current one (two slices ahead measured slower: the second
 // register set costs more occupancy than the latency it hides). Four waves in a 2 x 2 grid each own (BM/2) x
 // (BN/2) of the tile. out_proj's epilogue stages the tile through LDS, so
-// that the residual is read and the result written in whole rows. The last
-// tile of a row, which passes the sequence end, reads X entry by entry.
+// that the residual is read and the result written in whole rows. In the
+// last tile of a row, which passes the sequence end, the one 8-token chunk
+// per row that straddles the end is read and written entry by entry, and
+// the chunks past it are not touched; these tiles are dispatched first.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -108,7 +110,10 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         const uint32_t x = lin % kXcds, k = lin / kXcds, q = G / kXcds, r = G % kXcds;
         const uint32_t v = x * q + (x < r ? x : r) + k;
         mt = v % gx;
-        nt = (v / gx) % gy;
+        // token tiles in reverse order: a row's last tile, which passes the
+        // sequence end and reads its straddling chunks entry by entry, starts
+        // first instead of forming the kernel's tail
+        nt = gy - 1 - (v / gx) % gy;
         bt = v / (gx * gy);
     }
     const int m0 = mt * BM, n0 = nt * BN;
@@ -116,10 +121,26 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     const int M = a.M, K = a.K, L = a.L;
     const uint16_t* __restrict__ Xb = a.X + b * static_cast<int64_t>(K) * L;
 
-    // the tile's tokens all lie inside the sequence (uniform per workgroup);
-    // else X is read entry by entry, clamped (tokens past L feed only masked
-    // outputs)
+    // the tile's tokens all lie inside the sequence (uniform per workgroup).
+    // Else each 8-token chunk is read whole if it lies inside, entry by
+    // entry (clamped) if it straddles the end, and not at all past it: tokens
+    // past L feed only output columns that are never stored.
     const bool xwhole = n0 + BN <= L;
+    auto load_chunk = [&](const uint16_t* src, int t0) -> uint4 {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (xwhole || t0 + 8 <= L) {
+            __builtin_memcpy(&v, src + t0, 16);
+        } else if (t0 < L) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int u0 = t0 + 2 * e, u1 = u0 + 1;
+                w[e] = uint32_t(src[u0 < L ? u0 : L - 1]) | (uint32_t(src[u1 < L ? u1 : L - 1]) << 16);
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        return v;
+    };
 
     uint4 wreg[WVEC ? kChunkPT : 1];
     uint16_t wel[WVEC ? 1 : kElemPT];
@@ -149,17 +170,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
             const int r = c / (BN / 8), nc = (c % (BN / 8)) * 8;
             // rows past K: any finite value (W is zero there)
             const uint16_t* src = Xb + static_cast<int64_t>(k0 + r < K ? k0 + r : K - 1) * L;
-            if (xwhole) {
-                __builtin_memcpy(&xreg[i], src + n0 + nc, 16);
-            } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t0 = n0 + nc + 2 * e, t1 = t0 + 1;
-                    w[e] = uint32_t(src[t0 < L ? t0 : L - 1]) | (uint32_t(src[t1 < L ? t1 : L - 1]) << 16);
-                }
-                xreg[i] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
+            xreg[i] = load_chunk(src, n0 + nc);
         }
     };
     auto store_slice = [&]() {
@@ -234,8 +245,9 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     // accumulator r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
     if (EPI == kEpiOut) {
         // 1. the residual tile into LDS, 16 bytes (8 tokens of a row) per
-        //    load; the last tile of a row entry by entry, clamped (rows and
-        //    columns past the matrix: any valid element, never stored)
+        //    load; in the last tile of a row, a chunk that straddles the end
+        //    entry by entry, clamped (rows and columns past the matrix: any
+        //    valid element or zero, never stored)
         constexpr int kOutChunks = BM * BN / 8;
         static_assert(kOutChunks % kThreads == 0, "whole chunks per thread");
         constexpr int kOcpt = kOutChunks / kThreads;
@@ -246,19 +258,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
                 const int row = c / (BN / 8), nc = (c % (BN / 8)) * 8;
                 const int64_t mcl = m0 + row < M ? m0 + row : M - 1;
                 const uint16_t* src = a.res + (b * M + mcl) * static_cast<int64_t>(L);
-                uint4 v;
-                if (xwhole) {
-                    __builtin_memcpy(&v, src + n0 + nc, 16);
-                } else {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t0 = n0 + nc + 2 * e, t1 = t0 + 1;
-                        w[e] = uint32_t(src[t0 < L ? t0 : L - 1]) | (uint32_t(src[t1 < L ? t1 : L - 1]) << 16);
-                    }
-                    v = make_uint4(w[0], w[1], w[2], w[3]);
-                }
-                *reinterpret_cast<uint4*>(&sT[row][nc]) = v;
+                *reinterpret_cast<uint4*>(&sT[row][nc]) = load_chunk(src, n0 + nc);
             }
         }
         __syncthreads();
@@ -277,8 +277,8 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
                 }
             }
         __syncthreads();
-        // 3. the tile out, 16 bytes per store (the last tile of a row entry
-        //    by entry)
+        // 3. the tile out, 16 bytes per store (a chunk that straddles the
+        //    sequence end entry by entry; chunks past it are not stored)
 #pragma unroll
         for (int q = 0; q < kOcpt; ++q) {
             const int c = tid + q * kThreads;
@@ -286,9 +286,9 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
             if (m0 + row >= M) continue;
             uint16_t* dst = a.out + (b * M + m0 + row) * static_cast<int64_t>(L) + n0 + nc;
             const uint4 v = *reinterpret_cast<const uint4*>(&sT[row][nc]);
-            if (xwhole) {
+            if (xwhole || n0 + nc + 8 <= L) {
                 __builtin_memcpy(dst, &v, 16);
-            } else {
+            } else if (n0 + nc < L) {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
