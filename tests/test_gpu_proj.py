@@ -70,7 +70,8 @@ def test_dt_proj(shape):
 
 @pytest.mark.parametrize("bias,res", [(True, True), (False, False), (True, False), (False, True)])
 @pytest.mark.parametrize("shape", [(2, 64, 48, 37), (1, 100, 130, 200), (2, 256, 256, 300),
-                                   (1, 8, 3, 1), (2, 64, 160, 72), (1, 72, 64, 71)])
+                                   (1, 8, 3, 1), (2, 64, 160, 72), (1, 72, 64, 71),
+                                   (1, 64, 160, 1031), (2, 96, 136, 1100)])
 def test_out_proj(shape, bias, res):
     import vision_mamba_selective_amd as vms
     batch, din, dout, L = shape

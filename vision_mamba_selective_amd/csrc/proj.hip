@@ -23,9 +23,11 @@
 // to lane i of its group, so every lane receives 4 consecutive k of its own
 // token. The next slice is loaded into registers while the matrix cores
 // work on the current one (two slices ahead measured slower: the second
-// register set costs more occupancy than the latency it hides). Four waves in a 2 x 2 grid each own (BM/2) x
-// (BN/2) of the tile. out_proj's epilogue stages the tile through LDS, so
-// that the residual is read and the result written in whole rows. In the
+// register set costs more occupancy than the latency it hides). The
+// workgroup's 2 x WN waves each own (BM/2) x (BN/WN) of the tile: out_proj
+// takes 128 x 128 tiles in 8 waves, x_proj 64 x 64 tiles in 4. out_proj's
+// epilogue stages the tile through LDS, so that the residual is read and
+// the result written in whole rows. In the
 // last tile of a row, which passes the sequence end, the one 8-token chunk
 // per row that straddles the end is read and written entry by entry, and
 // the chunks past it are not touched; these tiles are dispatched first.
@@ -42,6 +44,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kThreads = 256;
+constexpr int64_t kWideTileMinL = 1024;    // out_proj: 128-token tiles from this length on
 constexpr int kXPad = 16;               // X slice rows: BN + 16 bf16, 160 bytes for BN = 64,
                                         // which puts the 4 rows x 2 token halves that a
                                         // transposing read touches per 32 lanes on
@@ -70,22 +73,28 @@ typedef __attribute__((ext_vector_type(4))) short v4s;
 
 // BK: K per LDS slice. W's slice rows are BK + 8 bf16 (16 bytes of padding),
 // which keeps the fragment reads of 16 lanes on distinct banks.
-template <int BM, int BN, int BK, int EPI, bool WVEC>
-__global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
-    static_assert(BM % 64 == 0 && BN % 64 == 0, "2 x 2 waves of 32 x 32 MFMA tiles");
+// WN: waves across the tile's tokens (2 across its rows), 2 x WN waves of
+// 64 lanes in the workgroup, each owning (BM / 2) x (BN / WN) of the tile.
+template <int BM, int BN, int BK, int EPI, bool WVEC, int WN>
+__global__ __launch_bounds__(128 * WN) void proj_gemm_kernel(const ProjArgs a) {
+    constexpr int kWgThreads = 128 * WN;
+    static_assert(BM % 64 == 0 && BN % (32 * WN) == 0, "2 x WN waves of 32 x 32 MFMA tiles");
     static_assert(BK % 16 == 0, "whole MFMA k steps per slice");
     constexpr int kBK = BK;
     constexpr int kRow = BK + 8;
-    constexpr int TM = BM / 64, TN = BN / 64;
+    constexpr int TM = BM / 64, TN = BN / (32 * WN);
     // X slice: kBK rows of BN tokens, 16-byte chunks of 8 tokens
-    constexpr int kXRow = BN + kXPad;
+    // rows of BN + 16 bf16 for BN = 64 and BN + 80 for multiples of 128: both
+    // are 40 dwords mod 64 banks, which keeps a transposing read's rows and
+    // token halves apart
+    constexpr int kXRow = BN + (BN >= 128 ? 80 : kXPad);
     constexpr int kXChunks = kBK * BN / 8;
-    static_assert(kXChunks % kThreads == 0, "whole chunks per thread");
-    constexpr int kXcpt = kXChunks / kThreads;
+    static_assert(kXChunks % kWgThreads == 0, "whole chunks per thread");
+    constexpr int kXcpt = kXChunks / kWgThreads;
     // W slice: 16-byte chunks (WVEC) or single elements
     constexpr int kChunks = BM * kBK / 8;
-    constexpr int kChunkPT = (kChunks + kThreads - 1) / kThreads;
-    constexpr int kElemPT = BM * kBK / kThreads;
+    constexpr int kChunkPT = (kChunks + kWgThreads - 1) / kWgThreads;
+    constexpr int kElemPT = BM * kBK / kWgThreads;
 
     // the operand slices; after the K loop the same memory holds the output
     // tile (bf16, rows of BN + 8), staged so that residual reads and result
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
     uint16_t (*sT)[kOutRow] = reinterpret_cast<uint16_t (*)[kOutRow]>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     // Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin by
     // linear id; renumber them so that each XCD runs one contiguous range of
     // tiles. Neighbouring M tiles read the same X columns, which then stay
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         if (WVEC) {
 #pragma unroll
             for (int i = 0; i < kChunkPT; ++i) {
-                const int c = tid + i * kThreads;
+                const int c = tid + i * kWgThreads;
                 const int r = c / (kBK / 8), kc = (c % (kBK / 8)) * 8;
                 uint4 v = make_uint4(0, 0, 0, 0);
                 if (c < kChunks && m0 + r < M && k0 + kc < K)
@@ -163,14 +172,14 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         } else {
 #pragma unroll
             for (int i = 0; i < kElemPT; ++i) {
-                const int e = tid + i * kThreads;
+                const int e = tid + i * kWgThreads;
                 const int r = e / kBK, kk = e % kBK;
                 wel[i] = (m0 + r < M && k0 + kk < K) ? a.W[static_cast<int64_t>(m0 + r) * K + k0 + kk] : 0;
             }
         }
 #pragma unroll
         for (int i = 0; i < kXcpt; ++i) {
-            const int c = tid + i * kThreads;
+            const int c = tid + i * kWgThreads;
             const int r = c / (BN / 8), nc = (c % (BN / 8)) * 8;
             // rows past K: any finite value (W is zero there)
             const uint16_t* src = Xb + static_cast<int64_t>(k0 + r < K ? k0 + r : K - 1) * L;
@@ -181,20 +190,20 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         if (WVEC) {
 #pragma unroll
             for (int i = 0; i < kChunkPT; ++i) {
-                const int c = tid + i * kThreads;
+                const int c = tid + i * kWgThreads;
                 if (c < kChunks)
                     *reinterpret_cast<uint4*>(&sA[c / (kBK / 8)][(c % (kBK / 8)) * 8]) = wreg[i];
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kElemPT; ++i) {
-                const int e = tid + i * kThreads;
+                const int e = tid + i * kWgThreads;
                 sA[e / kBK][e % kBK] = wel[i];
             }
         }
 #pragma unroll
         for (int i = 0; i < kXcpt; ++i) {
-            const int c = tid + i * kThreads;
+            const int c = tid + i * kWgThreads;
             *reinterpret_cast<uint4*>(&sX[c / (BN / 8)][(c % (BN / 8)) * 8]) = xreg[i];
         }
     };
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
                 fa[i] = *reinterpret_cast<const bf16x8*>(&sA[wm * (BM / 2) + i * 32 + fr][ks + fk]);
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int nb = wn * (BN / 2) + j * 32 + tn;
+                const int nb = wn * (BN / WN) + j * 32 + tn;
                 const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (__attribute__((address_space(3))) v4s*)(&sX[ks + tk][nb]));
                 const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -253,12 +262,12 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         //    entry by entry, clamped (rows and columns past the matrix: any
         //    valid element or zero, never stored)
         constexpr int kOutChunks = BM * BN / 8;
-        static_assert(kOutChunks % kThreads == 0, "whole chunks per thread");
-        constexpr int kOcpt = kOutChunks / kThreads;
+        static_assert(kOutChunks % kWgThreads == 0, "whole chunks per thread");
+        constexpr int kOcpt = kOutChunks / kWgThreads;
         if (a.res) {
 #pragma unroll
             for (int q = 0; q < kOcpt; ++q) {
-                const int c = tid + q * kThreads;
+                const int c = tid + q * kWgThreads;
                 const int row = c / (BN / 8), nc = (c % (BN / 8)) * 8;
                 const int64_t mcl = m0 + row < M ? m0 + row : M - 1;
                 const uint16_t* src = a.res + (b * M + mcl) * static_cast<int64_t>(L);
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int cn = wn * (BN / 2) + j * 32 + fr;
+                const int cn = wn * (BN / WN) + j * 32 + fr;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int cm = wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -285,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         //    sequence end entry by entry; chunks past it are not stored)
 #pragma unroll
         for (int q = 0; q < kOcpt; ++q) {
-            const int c = tid + q * kThreads;
+            const int c = tid + q * kWgThreads;
             const int row = c / (BN / 8), nc = (c % (BN / 8)) * 8;
             if (m0 + row >= M) continue;
             uint16_t* dst = a.out + (b * M + m0 + row) * static_cast<int64_t>(L) + n0 + nc;
@@ -306,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void proj_gemm_kernel(const ProjArgs a) {
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
-                const int n = n0 + wn * (BN / 2) + j * 32 + fr;
+                const int n = n0 + wn * (BN / WN) + j * 32 + fr;
                 if (n >= L) continue;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -369,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void dt_proj_kernel(const float* __restri
 
 using vs::fail;
 
-template <int BM, int BN, int BK, int EPI>
+template <int BM, int BN, int BK, int EPI, int WN>
 int launch(const ProjArgs& a, int64_t batch, hipStream_t st) {
     const int64_t tiles_l = (static_cast<int64_t>(a.L) + BN - 1) / BN;
     if (tiles_l > 65535)
@@ -378,9 +387,9 @@ int launch(const ProjArgs& a, int64_t batch, hipStream_t st) {
                     static_cast<unsigned>(batch));
     const bool wvec = a.K % 8 == 0 && vs::aligned(a.W, 16);
     if (wvec)
-        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, BK, EPI, true>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, BK, EPI, true, WN>), grid, dim3(128 * WN), 0, st, a);
     else
-        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, BK, EPI, false>), grid, dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((proj_gemm_kernel<BM, BN, BK, EPI, false, WN>), grid, dim3(128 * WN), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VS_ERR_HIP, hipGetErrorString(e));
     return VS_OK;
@@ -405,7 +414,7 @@ int vim_x_proj(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int d
     a.N = static_cast<int>(dstate); a.L = static_cast<int>(seqlen);
     // 128-deep slices: same output bits as 64-deep ones, 14.4 against 15.6 us
     // at 197 tokens (batch 64), 19.8 against 20.1 us at 4,097 (batch 8)
-    return launch<64, 64, 128, kEpiXproj>(a, batch, static_cast<hipStream_t>(stream));
+    return launch<64, 64, 128, kEpiXproj, 2>(a, batch, static_cast<hipStream_t>(stream));
 }
 
 int vim_dt_proj(int64_t batch, int64_t dim, int64_t seqlen, int dtype, const float* dt,
@@ -434,7 +443,15 @@ int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen,
     a.res = static_cast<const uint16_t*>(residual);
     a.out = static_cast<uint16_t*>(out);
     a.M = static_cast<int>(dim_out); a.K = static_cast<int>(dim_in); a.L = static_cast<int>(seqlen);
-    return launch<128, 64, 64, kEpiOut>(a, batch, static_cast<hipStream_t>(stream));
+    // Long sequences take 128 x 128 tiles in eight waves (each 64 x 32, as in
+    // the 128 x 64 tiles of four waves): W is read once per 128 tokens
+    // instead of 64, and twice the matrix work sits between a slice's
+    // barriers; same output bits, 91.9 against 94.1 us at 4,097 tokens
+    // (batch 8) and 74.9 against 81.2 at 4,096. Short ones keep 128 x 64:
+    // at 197 tokens (batch 64) the wider tile took 68 against 54 us.
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (seqlen >= kWideTileMinL) return launch<128, 128, 64, kEpiOut, 4>(a, batch, st);
+    return launch<128, 64, 64, kEpiOut, 2>(a, batch, st);
 }
 
 }  // extern "C"
