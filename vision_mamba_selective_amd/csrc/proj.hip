@@ -14,10 +14,10 @@
 // BM x BN tiles with v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
 // accumulation), which takes 8 consecutive k of one row of W (A) and of one
 // column of X (B) per lane. Per slice of K (64 deep for out_proj, 128 for
-// x_proj), W's rows are copied to
-// LDS as they are (k contiguous), and X's rows too (token contiguous), 16
-// bytes per load: X rows start at any 2-byte boundary (L is odd), which the
-// target's unaligned global access handles. The B fragments come out of LDS
+// x_proj), W's rows are copied to LDS as they are (k contiguous), and X's
+// rows too (token contiguous), 16 bytes per load: X rows start at any 2-byte
+// boundary (L is odd), which the target's unaligned global access handles.
+// The B fragments come out of LDS
 // with ds_read_b64_tr_b16, which transposes 4 x 16 blocks of b16 within each
 // 16-lane group: a lane reading 4 tokens of one k row contributes element i
 // to lane i of its group, so every lane receives 4 consecutive k of its own
@@ -25,12 +25,13 @@
 // work on the current one (two slices ahead measured slower: the second
 // register set costs more occupancy than the latency it hides). The
 // workgroup's 2 x WN waves each own (BM/2) x (BN/WN) of the tile: out_proj
-// takes 128 x 128 tiles in 8 waves, x_proj 64 x 64 tiles in 4. out_proj's
-// epilogue stages the tile through LDS, so that the residual is read and
-// the result written in whole rows. In the
-// last tile of a row, which passes the sequence end, the one 8-token chunk
-// per row that straddles the end is read and written entry by entry, and
-// the chunks past it are not touched; these tiles are dispatched first.
+// takes 128 x 128 tiles in 8 waves from 1,024 tokens on (128 x 64 in 4
+// below), x_proj 64 x 64 tiles in 4. out_proj's epilogue stages the tile
+// through LDS, so that the residual is read and the result written in whole
+// rows. In the last tile of a row, which passes the sequence end, the one
+// 8-token chunk per row that straddles the end is read and written entry by
+// entry, and the chunks past it are not touched; these tiles are dispatched
+// first.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
