@@ -13,10 +13,11 @@
 // proj_gemm_kernel computes one batch row's Out[M][L] = W[M][K] X[K][L] in
 // BM x BN tiles with v_mfma_f32_32x32x16_bf16 (bf16 operands, fp32
 // accumulation), which takes 8 consecutive k of one row of W (A) and of one
-// column of X (B) per lane. Per slice of K (64 deep for out_proj, 128 for
-// x_proj), W's rows are copied to LDS as they are (k contiguous), and X's
-// rows too (token contiguous), 16 bytes per load: X rows start at any 2-byte
-// boundary (L is odd), which the target's unaligned global access handles.
+// column of X (B) per lane. Per slice of K (128 deep, 64 for out_proj's
+// short-sequence tile), W's rows are copied to LDS as they are (k
+// contiguous), and X's rows too (token contiguous), 16 bytes per load: X
+// rows start at any 2-byte boundary (L is odd), which the target's
+// unaligned global access handles.
 // The B fragments come out of LDS
 // with ds_read_b64_tr_b16, which transposes 4 x 16 blocks of b16 within each
 // 16-lane group: a lane reading 4 tokens of one k row contributes element i
@@ -85,10 +86,10 @@ __global__ __launch_bounds__(128 * WN) void proj_gemm_kernel(const ProjArgs a) {
     constexpr int kRow = BK + 8;
     constexpr int TM = BM / 64, TN = BN / (32 * WN);
     // X slice: kBK rows of BN tokens, 16-byte chunks of 8 tokens
-    // rows of BN + 16 bf16 for BN = 64 and BN + 80 for multiples of 128: both
-    // are 40 dwords mod 64 banks, which keeps a transposing read's rows and
-    // token halves apart
-    constexpr int kXRow = BN + (BN >= 128 ? 80 : kXPad);
+    // rows of BN + 16 bf16 for BN = 64 (40 dwords mod 64 banks) and BN + 32
+    // for BN = 128 (16 dwords mod 64: the 4 rows of a transposing read, 16
+    // dwords each with both token halves, fill the 64 banks once)
+    constexpr int kXRow = BN + (BN >= 128 ? 32 : kXPad);
     constexpr int kXChunks = kBK * BN / 8;
     static_assert(kXChunks % kWgThreads == 0, "whole chunks per thread");
     constexpr int kXcpt = kXChunks / kWgThreads;
@@ -445,13 +446,13 @@ int vim_out_proj(int64_t batch, int64_t dim_in, int64_t dim_out, int64_t seqlen,
     a.out = static_cast<uint16_t*>(out);
     a.M = static_cast<int>(dim_out); a.K = static_cast<int>(dim_in); a.L = static_cast<int>(seqlen);
     // Long sequences take 128 x 128 tiles in eight waves (each 64 x 32, as in
-    // the 128 x 64 tiles of four waves): W is read once per 128 tokens
-    // instead of 64, and twice the matrix work sits between a slice's
-    // barriers; same output bits, 91.9 against 94.1 us at 4,097 tokens
-    // (batch 8) and 74.9 against 81.2 at 4,096. Short ones keep 128 x 64:
-    // at 197 tokens (batch 64) the wider tile took 68 against 54 us.
+    // the 128 x 64 tiles of four waves) and 128-deep K slices: W is read once
+    // per 128 tokens instead of 64, a workgroup has 64 KB of operands in
+    // flight per slice, and four times the matrix work sits between a
+    // slice's barriers; same output bits. Short sequences keep 128 x 64
+    // tiles: at 197 tokens (batch 64) the wider tile took 68 against 54 us.
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (seqlen >= kWideTileMinL) return launch<128, 128, 64, kEpiOut, 4>(a, batch, st);
+    if (seqlen >= kWideTileMinL) return launch<128, 128, 128, kEpiOut, 4>(a, batch, st);
     return launch<128, 64, 64, kEpiOut, 2>(a, batch, st);
 }
 
