@@ -40,7 +40,7 @@ def operands(rng, batch, K, M, L):
 
 
 @pytest.mark.parametrize("shape", [(2, 24, 16, 37), (1, 100, 16, 130), (3, 8, 8, 65),
-                                   (1, 64, 4, 1)])
+                                   (1, 64, 4, 1), (2, 200, 16, 300), (1, 136, 8, 70)])
 def test_x_proj(shape):
     import vision_mamba_selective_amd as vms
     batch, dim, N, L = shape
@@ -71,7 +71,8 @@ def test_dt_proj(shape):
 @pytest.mark.parametrize("bias,res", [(True, True), (False, False), (True, False), (False, True)])
 @pytest.mark.parametrize("shape", [(2, 64, 48, 37), (1, 100, 130, 200), (2, 256, 256, 300),
                                    (1, 8, 3, 1), (2, 64, 160, 72), (1, 72, 64, 71),
-                                   (1, 64, 160, 1031), (2, 96, 136, 1100)])
+                                   (1, 64, 160, 1031), (2, 96, 136, 1100), (1, 200, 96, 1100),
+                                   (1, 136, 130, 1030)])
 def test_out_proj(shape, bias, res):
     import vision_mamba_selective_amd as vms
     batch, din, dout, L = shape
